@@ -1,0 +1,214 @@
+"""NVFP4 W4A4 linear layer and NVFP4 KV cache for one MI355X (gfx950).
+
+Thin torch-facing binding over the C ABI in ``include/nvfp4.h`` (``libnvfp4.so``):
+the functions here only check tensor shapes / dtypes / devices, allocate
+outputs as torch tensors and pass raw pointers plus the current HIP stream.
+Every step of the computation runs in the library's HIP kernels.
+
+Method: "LongLive-2.0：用 NVFP4 并行底座做长视频生成" (yingwang.github.io), 二、方法 /
+NVFP4 量化格式 (E2M1 elements, E4M3 per-16 block scales, FP32 tensor scale) and
+二、方法 / 推理底座 (W4A4 inference, NVFP4 KV cache).
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import torch
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    NVFP4_EPI_GELU_TANH,
+    NVFP4_TILES,
+    KVCacheDesc,
+    NVFP4Error,
+    check,
+    header_symbols,
+    lib,
+)
+
+__all__ = ["quantize", "quantize_into", "gemm", "linear", "KVCache", "NVFP4Error", "lib",
+           "gemm_tile", "quantize_workspace_bytes", "linear_workspace_bytes"]
+
+
+def _stream(device=None):
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the NVFP4 kernels run only on the GPU)")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def quantize_workspace_bytes(M: int, K: int) -> int:
+    n = C.c_size_t()
+    check(lib().nvfp4_quantize_workspace(M, K, C.byref(n)))
+    return n.value
+
+
+def linear_workspace_bytes(M: int, K: int) -> int:
+    n = C.c_size_t()
+    check(lib().nvfp4_linear_workspace(M, K, C.byref(n)))
+    return n.value
+
+
+def quantize_into(x, codes, scales, gscale, ws):
+    """nvfp4_quantize into caller-provided tensors (no allocation)."""
+    M, K = x.shape
+    _need(x, torch.bfloat16, "x")
+    _need(codes, torch.uint8, "codes", (M, K // 2))
+    _need(scales, torch.uint8, "scales", (M, K // 16))
+    _need(gscale, torch.float32, "gscale", (1,))
+    _need(ws, torch.uint8, "ws")
+    check(lib().nvfp4_quantize(_ptr(x), M, K, _ptr(codes), _ptr(scales), _ptr(gscale),
+                               _ptr(ws), ws.numel(), _stream(x.device)))
+
+
+def quantize(x: torch.Tensor):
+    """bf16 [M, K] → (codes u8 [M, K/2], scales u8 [M, K/16], gscale f32 [1])."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    dev = x.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    gscale = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = torch.empty((quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+    quantize_into(x, codes, scales, gscale, ws)
+    return codes, scales, gscale
+
+
+def _flags(gelu, tile):
+    f = NVFP4_EPI_GELU_TANH if gelu else 0
+    if tile is not None:
+        f |= NVFP4_TILES[tuple(tile)]
+    return f
+
+
+def gemm(Aq, As, Ag, Wq, Ws, Wg, bias=None, gelu=False, out=None, tile=None):
+    """W4A4 GEMM: NVFP4 A [M, K] times NVFP4 Wᵀ ([N, K]) → bf16 [M, N].
+
+    ``tile`` optionally forces the workgroup tile, e.g. (256, 192)."""
+    M, K2 = Aq.shape
+    N = Wq.shape[0]
+    K = 2 * K2
+    _need(Aq, torch.uint8, "Aq")
+    _need(As, torch.uint8, "As", (M, K // 16))
+    _need(Ag, torch.float32, "Ag", (1,))
+    _need(Wq, torch.uint8, "Wq", (N, K // 2))
+    _need(Ws, torch.uint8, "Ws", (N, K // 16))
+    _need(Wg, torch.float32, "Wg", (1,))
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", (N,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=Aq.device)
+    _need(out, torch.bfloat16, "out", (M, N))
+    flags = _flags(gelu, tile)
+    check(lib().nvfp4_gemm(_ptr(Aq), _ptr(As), _ptr(Ag), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias),
+                           _ptr(out), M, N, K, flags, _stream(Aq.device)))
+    return out
+
+
+def linear(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, ws=None, tile=None):
+    """The W4A4 linear layer: quantise bf16 x [M, K] per call, then GEMM with
+    pre-quantised weights.  ``ws`` (uint8, ≥ linear_workspace_bytes) may be
+    passed to avoid an allocation per call."""
+    M, K = x.shape
+    N = Wq.shape[0]
+    _need(x, torch.bfloat16, "x")
+    _need(Wq, torch.uint8, "Wq", (N, K // 2))
+    _need(Ws, torch.uint8, "Ws", (N, K // 16))
+    _need(Wg, torch.float32, "Wg", (1,))
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", (N,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out", (M, N))
+    if ws is None:
+        ws = torch.empty((linear_workspace_bytes(M, K),), dtype=torch.uint8, device=x.device)
+    _need(ws, torch.uint8, "ws")
+    flags = _flags(gelu, tile)
+    check(lib().nvfp4_linear(_ptr(x), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias), _ptr(out),
+                             M, N, K, flags, _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+class KVCache:
+    """NVFP4 KV cache with device buffers held as torch tensors.
+
+    ``append(K, V)`` quantises a chunk of bf16 [T, heads, head_dim] keys and
+    values into the cache (one pair of tensor scales per append);
+    ``dequant(t0, t1)`` returns bf16 K and V for tokens [t0, t1).
+    """
+
+    def __init__(self, capacity: int, heads: int, head_dim: int, max_chunks: int, device="cuda"):
+        dev = torch.device(device)
+        self.k_codes = torch.zeros((capacity, heads, head_dim // 2), dtype=torch.uint8, device=dev)
+        self.v_codes = torch.zeros_like(self.k_codes)
+        self.k_scales = torch.zeros((capacity, heads, head_dim // 16), dtype=torch.uint8, device=dev)
+        self.v_scales = torch.zeros_like(self.k_scales)
+        self.gscale = torch.zeros((max_chunks, 2), dtype=torch.float32, device=dev)
+        self.chunk_start = torch.zeros((max_chunks + 1,), dtype=torch.int64, device=dev)
+        self.desc = KVCacheDesc(capacity, heads, head_dim, max_chunks,
+                                self.k_codes.data_ptr(), self.k_scales.data_ptr(),
+                                self.v_codes.data_ptr(), self.v_scales.data_ptr(),
+                                self.gscale.data_ptr(), self.chunk_start.data_ptr(), 0, 0)
+        check(lib().nvfp4_kv_init(C.byref(self.desc)))
+        self.device = dev
+        self._ws = None
+
+    @property
+    def n_tokens(self):
+        return self.desc.n_tokens
+
+    @property
+    def n_chunks(self):
+        return self.desc.n_chunks
+
+    def workspace_bytes(self, T: int) -> int:
+        n = C.c_size_t()
+        check(lib().nvfp4_kv_append_workspace(T, self.desc.heads, self.desc.head_dim, C.byref(n)))
+        return n.value
+
+    def append(self, K, V, ws=None):
+        T = K.shape[0]
+        shape = (T, self.desc.heads, self.desc.head_dim)
+        _need(K, torch.bfloat16, "K", shape)
+        _need(V, torch.bfloat16, "V", shape)
+        if ws is None:
+            if self._ws is None or self._ws.numel() < self.workspace_bytes(T):
+                self._ws = torch.empty((self.workspace_bytes(T),), dtype=torch.uint8, device=self.device)
+            ws = self._ws
+        check(lib().nvfp4_kv_append(C.byref(self.desc), _ptr(K), _ptr(V), T, _ptr(ws), ws.numel(),
+                                    _stream(self.device)))
+
+    def dequant(self, t0: int, t1: int, k_out=None, v_out=None):
+        shape = (t1 - t0, self.desc.heads, self.desc.head_dim)
+        if k_out is None:
+            k_out = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        if v_out is None:
+            v_out = torch.empty(shape, dtype=torch.bfloat16, device=self.device)
+        _need(k_out, torch.bfloat16, "k_out", shape)
+        _need(v_out, torch.bfloat16, "v_out", shape)
+        check(lib().nvfp4_kv_dequant(C.byref(self.desc), t0, t1, _ptr(k_out), _ptr(v_out),
+                                     _stream(self.device)))
+        return k_out, v_out
+
+
+def gemm_tile(M: int, N: int, K: int) -> tuple:
+    """Workgroup tile (BM, BN) the library uses for an M x N x K GEMM."""
+    bm, bn = C.c_int(), C.c_int()
+    check(lib().nvfp4_gemm_tile(M, N, K, C.byref(bm), C.byref(bn)))
+    return bm.value, bn.value

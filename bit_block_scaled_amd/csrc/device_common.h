@@ -1,0 +1,72 @@
+// Device helpers shared by the NVFP4 kernels (gfx950 only).
+//
+// Format facts used here ("LongLive-2.0：用 NVFP4 并行底座做长视频生成",
+// 二、方法 / NVFP4 量化格式): elements are E2M1, block scales FP8 E4M3 (one per
+// 16 elements), the tensor scale FP32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr float kGlobalDivisor = 2688.0f;   // 6 (largest E2M1) · 448 (largest E4M3)
+constexpr float kE2M1Max = 6.0f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Nearest-even E4M3 ("FN": bias 7, max 448) encoding of a finite s >= 0, with
+// saturation to 448.  Normal range: round the binary32 bit pattern to 3
+// mantissa bits (the carry runs into the exponent); below 2^-6 the grid is the
+// fixed quantum 2^-9, so the byte is the nearest-even integer of s·2^9.
+__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float s) {
+  if (s >= 448.0f) return 0x7Eu;
+  if (s < 0.015625f) {                       // 2^-6
+    float t = s * 512.0f;                    // exact
+    return (uint32_t)__builtin_rintf(t);     // 0..8, 8 = 2^-6 = byte 0x08
+  }
+  uint32_t u = __float_as_uint(s);
+  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;   // RNE to 3 mantissa bits
+  uint32_t b = r - (120u << 3);              // rebias exponent 127 → 7
+  return b > 0x7Eu ? 0x7Eu : b;
+}
+
+// E4M3 byte → float (exact), OCP decoding of the hardware converter.
+__device__ __forceinline__ float e4m3_decode(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+}
+
+// bf16 pair from two floats, nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Largest bf16 magnitude (as its 15-bit pattern) in a dword pair-wise.
+__device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t acc, uint32_t v) {
+  typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+  u16x2 a = __builtin_bit_cast(u16x2, acc);
+  u16x2 b = __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+}  // namespace nvfp4

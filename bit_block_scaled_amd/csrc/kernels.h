@@ -1,0 +1,67 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Upper bound on the number of amax partials one quantisation writes.
+constexpr int kAmaxBlocks = 1024;
+
+// One tensor to quantise: `elements` bf16 values (a multiple of 32) from x to
+// codes (elements/2 bytes), scales (elements/16 bytes) and *gscale, using
+// `partials` (kAmaxBlocks uint32) as scratch.
+struct QuantJob {
+  const uint16_t *x;
+  uint8_t *codes;
+  uint8_t *scales;
+  float *gscale;
+  uint32_t *partials;
+  int64_t elements;
+};
+
+// KV-cache bookkeeping written by the encode launch of an append:
+// chunk_start[index] = value (and chunk_start[0] = 0 when index == 1).
+struct ChunkMark {
+  int64_t *chunk_start;
+  int64_t index;
+  int64_t value;
+};
+
+// Quantises one or two tensors (njobs in {1, 2}) with two launches on `stream`.
+hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
+                           const ChunkMark *mark = nullptr);
+
+struct GemmArgs {
+  const uint8_t *Aq;
+  const uint8_t *As;
+  const float *Ag;
+  const uint8_t *Wq;
+  const uint8_t *Ws;
+  const float *Wg;
+  const uint16_t *bias;
+  uint16_t *C;
+  int64_t M, N, K;
+  uint32_t flags;
+};
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
+
+// Tile shape chosen for a problem (exposed for the benchmark's reporting).
+void gemm_tile_for(int64_t M, int64_t N, int64_t K, int *bm, int *bn);
+
+struct KvDequantArgs {
+  const uint8_t *codes[2];
+  const uint8_t *scales[2];
+  uint16_t *out[2];
+  const float *gscale;          // [chunks, 2]
+  const int64_t *chunk_start;   // [chunks + 1]
+  int64_t n_chunks;
+  int64_t t0, t1;
+  int64_t elems_per_token;      // heads · head_dim (multiple of 32)
+};
+
+hipError_t launch_kv_dequant(const KvDequantArgs &a, hipStream_t stream);
+
+}  // namespace nvfp4

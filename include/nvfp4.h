@@ -1,0 +1,199 @@
+/*
+ * nvfp4.h — C ABI of the MI355X (gfx950) NVFP4 W4A4 linear layer and NVFP4
+ * KV cache.
+ *
+ * Method: "LongLive-2.0：用 NVFP4 并行底座做长视频生成" (yingwang.github.io
+ * reading notes), section 二、方法:
+ *   - NVFP4 量化格式: a tensor is stored as E2M1 4-bit elements, one FP8 E4M3
+ *     scale per 16 contiguous elements and one FP32 scale per tensor;
+ *     Dequant(X) = X^FP4 · α^FP8 · α^FP32.
+ *   - NVFP4 训练的工程细节: weights and activations are both 4-bit (W4A4);
+ *     activations use 1-D block scaling; reductions stay in higher precision.
+ *   - 推理底座: weights are materialised once in 4 bits; the KV cache is
+ *     quantised again per chunk (4·T·H·d → 9/8·T·H·d bytes) and read back
+ *     through a dequantisation kernel.
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  bf16 values travel as uint16_t
+ *     bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work; none synchronises the host.  Results (including
+ *     the FP32 tensor scale) stay in device memory.
+ *   - Return value: NVFP4_OK (0) or a positive status code.  Argument errors are
+ *     detected on the host before anything is enqueued and leave every output
+ *     untouched.  A kernel fault surfaces at the caller's next synchronisation.
+ *     No C++ exception crosses this interface.  nvfp4_last_error() gives a
+ *     message for the calling thread's last failure.
+ *   - Preconditions not checked on the device: bf16 inputs are finite and a
+ *     tensor's largest magnitude is 0 or at least 2^-100.
+ *   - Layouts are row-major and dense.  A row of K elements occupies K/2 code
+ *     bytes (element 2j in the low nibble of byte j) and K/16 scale bytes
+ *     (E4M3, block b covers elements 16b..16b+15).
+ *   - Concurrency: calls are reentrant; calls that share an output buffer or a
+ *     KV cache must be ordered by the caller (same stream, or events).
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define NVFP4_OK          0
+#define NVFP4_EINVAL      1  /* null pointer, bad size, misalignment, unknown flag */
+#define NVFP4_EWORKSPACE  2  /* workspace missing or smaller than required       */
+#define NVFP4_ECAPACITY   3  /* KV cache token capacity or chunk slots exhausted */
+#define NVFP4_EHIP        4  /* the HIP runtime reported an error at launch      */
+
+/* flags for nvfp4_gemm / nvfp4_linear */
+#define NVFP4_EPI_GELU_TANH 0x1u  /* apply tanh-form GELU before the bf16 cast */
+/* Optional workgroup-tile choice (a performance hint; 0 = automatic).  The
+ * result does not depend on it beyond fp32 summation order. */
+#define NVFP4_TILE_MASK     0xF00u
+#define NVFP4_TILE_256x256  0x100u
+#define NVFP4_TILE_256x192  0x200u
+#define NVFP4_TILE_192x256  0x300u
+#define NVFP4_TILE_256x128  0x400u
+#define NVFP4_TILE_128x256  0x500u
+#define NVFP4_TILE_128x128  0x600u
+
+/* Alignment every device pointer must satisfy (bytes). */
+#define NVFP4_ALIGN 16
+
+/*
+ * Workspace bytes nvfp4_quantize needs for an [M, K] input (scratch for the
+ * tensor-amax reduction).  Writes *bytes; the size depends only on M and K.
+ */
+int nvfp4_quantize_workspace(int64_t M, int64_t K, size_t *bytes);
+
+/*
+ * Dynamic NVFP4 quantisation of a bf16 matrix (the per-call activation
+ * quantiser of W4A4 inference; also the offline weight quantiser).
+ * Source: 二、方法 / NVFP4 量化格式 (three-level scaling) and
+ * NVFP4 训练的工程细节 (1-D block scaling of activations).
+ *
+ *   x       bf16 [M, K] row-major, 16-byte aligned
+ *   codes   out: uint8 [M, K/2]   E2M1 codes, two per byte
+ *   scales  out: uint8 [M, K/16]  E4M3 block scales
+ *   gscale  out: float [1]        FP32 tensor scale g
+ *   ws      scratch of at least nvfp4_quantize_workspace(M, K) bytes
+ *
+ * Arithmetic (binary32, nearest-even, subnormals kept): A = max|x|;
+ * g = A/2688 (g = 1 when A = 0); per 16-block S = E4M3_rne_satfinite(a/(6g));
+ * r = 1/(S·g) (0 when S = 0); code = sign(x)·8 | E2M1_rne_sat(|x|·r).
+ * Requires M >= 1, K >= 32, K % 32 == 0.
+ */
+int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K,
+                   uint8_t *codes, uint8_t *scales, float *gscale,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * W4A4 GEMM with FP32 accumulation and a bf16 epilogue:
+ *   C[m, n] = bf16( fl32( fl32(acc[m, n] · fl32(Ag·Wg)) + bias[n] ) [→ GELU] )
+ *   acc[m, n] = Σ_k (E2M1(Aq[m,k])·E4M3(As[m,k/16])) · (E2M1(Wq[n,k])·E4M3(Ws[n,k/16]))
+ * Source: 二、方法 / NVFP4 量化格式 (Dequant = X^FP4·α^FP8·α^FP32) and
+ * 推理底座 (W4A4 inference with weights materialised once in 4 bits).
+ *
+ *   Aq, As, Ag  activations: codes [M, K/2], scales [M, K/16], tensor scale [1]
+ *   Wq, Ws, Wg  weights (one output channel per row): codes [N, K/2],
+ *               scales [N, K/16], tensor scale [1]
+ *   bias        bf16 [N] or NULL
+ *   C           out: bf16 [M, N] row-major
+ *   flags       NVFP4_EPI_GELU_TANH and/or one NVFP4_TILE_* hint (or 0)
+ * Requires M, N >= 1, K >= 32, K % 32 == 0.  Every scale byte must be a
+ * finite E4M3 value (not 0x7F/0xFF).
+ */
+int nvfp4_gemm(const uint8_t *Aq, const uint8_t *As, const float *Ag,
+               const uint8_t *Wq, const uint8_t *Ws, const float *Wg,
+               const uint16_t *bias, uint16_t *C,
+               int64_t M, int64_t N, int64_t K, uint32_t flags, void *stream);
+
+/*
+ * Workgroup tile (rows of A x rows of W) nvfp4_gemm uses for an M x N x K
+ * problem; informational (for reporting), enqueues nothing.
+ */
+int nvfp4_gemm_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn);
+
+/* Workspace bytes nvfp4_linear needs for an [M, K] activation. */
+int nvfp4_linear_workspace(int64_t M, int64_t K, size_t *bytes);
+
+/*
+ * The W4A4 linear layer: nvfp4_quantize(x) into the workspace, then
+ * nvfp4_gemm against pre-quantised weights, on one stream.
+ *   x   bf16 [M, K];  other arguments as for nvfp4_gemm;
+ *   ws  scratch of at least nvfp4_linear_workspace(M, K) bytes.
+ */
+int nvfp4_linear(const uint16_t *x,
+                 const uint8_t *Wq, const uint8_t *Ws, const float *Wg,
+                 const uint16_t *bias, uint16_t *C,
+                 int64_t M, int64_t N, int64_t K, uint32_t flags,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * NVFP4 KV cache.  Source: 二、方法 / 推理底座 (the KV cache is quantised per
+ * chunk in place and read back through a dequantisation kernel; storage
+ * 9/8·T·H·d bytes for K and V together).
+ *
+ * The caller allocates the device buffers and fills the geometry and pointer
+ * fields; nvfp4_kv_init validates them and zeroes the counters.  The counters
+ * are host-side state maintained by the library; do not edit them.  Each
+ * append quantises K and V (each viewed as [T·H, head_dim], blocks of 16
+ * along head_dim) with its own pair of tensor scales and writes them at token
+ * offset n_tokens.
+ */
+typedef struct nvfp4_kv_cache {
+    int64_t capacity;      /* tokens the buffers hold                        */
+    int64_t heads;         /* H                                              */
+    int64_t head_dim;      /* d, multiple of 32                              */
+    int64_t max_chunks;    /* appends the gscale / chunk_start arrays hold   */
+    uint8_t *k_codes;      /* device [capacity, heads, head_dim/2]           */
+    uint8_t *k_scales;     /* device [capacity, heads, head_dim/16]          */
+    uint8_t *v_codes;      /* device [capacity, heads, head_dim/2]           */
+    uint8_t *v_scales;     /* device [capacity, heads, head_dim/16]          */
+    float *gscale;         /* device [max_chunks, 2]: (g_K, g_V) per append  */
+    int64_t *chunk_start;  /* device [max_chunks + 1]: first token per chunk */
+    int64_t n_tokens;      /* host counter: tokens written                   */
+    int64_t n_chunks;      /* host counter: appends made                     */
+} nvfp4_kv_cache;
+
+/* Validate geometry and pointers, zero the counters.  Enqueues nothing. */
+int nvfp4_kv_init(nvfp4_kv_cache *c);
+
+/* Workspace bytes nvfp4_kv_append needs for an append of T tokens. */
+int nvfp4_kv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t *bytes);
+
+/*
+ * Quantise K and V (bf16 [T, heads, head_dim]) into the cache at token offset
+ * c->n_tokens, record their tensor scales as chunk c->n_chunks, then advance
+ * the counters.  Returns NVFP4_ECAPACITY (cache unchanged) when the tokens or
+ * the chunk slots would overflow.  T >= 1.
+ */
+int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Dequantise tokens [t0, t1) of K and V to bf16 [t1-t0, heads, head_dim]:
+ *   out = bf16( fl32( fl32(E2M1 · E4M3) · g_chunk ) )
+ * (the first product is exact; g_chunk is the tensor scale of the append that
+ * wrote the token).  Requires 0 <= t0 <= t1 <= c->n_tokens; t0 == t1 is a no-op
+ * (the output pointers are then not used and may be NULL).
+ */
+int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1,
+                     uint16_t *K_out, uint16_t *V_out, void *stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *nvfp4_strerror(int status);
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char *nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

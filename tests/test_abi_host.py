@@ -1,0 +1,177 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/nvfp4.h declares, and
+reject every invalid argument on the host — with the documented status code,
+before anything is enqueued.  No call here passes validation: pointers are
+fake addresses that are never dereferenced.
+"""
+
+import ctypes as C
+import os
+import subprocess
+
+import pytest
+
+import bit_block_scaled_amd as nv
+from bit_block_scaled_amd import _lib
+
+EINVAL, EWS, ECAP = _lib.NVFP4_EINVAL, _lib.NVFP4_EWORKSPACE, _lib.NVFP4_ECAPACITY
+
+FAKE = 0x100000           # 16-byte aligned, never dereferenced
+MIS = FAKE + 8            # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail(f"{_lib.LIB_PATH} not built (run __graft_entry__.build())")
+    return nv.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _lib.header_symbols()
+    assert len(declared) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for s in declared:
+        assert getattr(L, s) is not None
+
+
+def test_strerror(L):
+    assert L.nvfp4_strerror(0) == b"ok"
+    assert b"invalid" in L.nvfp4_strerror(EINVAL)
+    assert b"workspace" in L.nvfp4_strerror(EWS)
+    assert b"capacity" in L.nvfp4_strerror(ECAP)
+    assert L.nvfp4_strerror(99) == b"unknown status"
+
+
+def _ws(L, M, K):
+    n = C.c_size_t()
+    return L.nvfp4_quantize_workspace(M, K, C.byref(n)), n.value
+
+
+def test_workspace_queries(L):
+    s, n = _ws(L, 4096, 3072)
+    assert s == 0 and n >= 4096
+    assert _ws(L, 4096, 48)[0] == EINVAL
+    assert _ws(L, 0, 64)[0] == EINVAL
+    assert L.nvfp4_quantize_workspace(4, 64, None) == EINVAL
+    n = C.c_size_t()
+    assert L.nvfp4_linear_workspace(4096, 3072, C.byref(n)) == 0
+    assert n.value >= 4096 * 3072 // 2 + 4096 * 3072 // 16
+    assert L.nvfp4_kv_append_workspace(880, 24, 128, C.byref(n)) == 0 and n.value > 0
+    assert L.nvfp4_kv_append_workspace(880, 24, 100, C.byref(n)) == EINVAL
+    bm, bn = C.c_int(), C.c_int()
+    assert L.nvfp4_gemm_tile(4096, 9216, 3072, C.byref(bm), C.byref(bn)) == 0
+    assert bm.value % 64 == 0 and bn.value % 64 == 0
+
+
+def _q(L, x=FAKE, M=64, K=64, codes=FAKE, scales=FAKE, g=FAKE, ws=FAKE, wsb=1 << 20):
+    return L.nvfp4_quantize(x, M, K, codes, scales, g, ws, wsb, None)
+
+
+def test_quantize_rejects(L):
+    assert _q(L, x=None) == EINVAL
+    assert _q(L, codes=None) == EINVAL
+    assert _q(L, x=MIS) == EINVAL
+    assert _q(L, scales=MIS) == EINVAL
+    assert _q(L, K=48) == EINVAL            # K % 32
+    assert _q(L, K=16) == EINVAL
+    assert _q(L, M=0) == EINVAL
+    assert _q(L, M=-5) == EINVAL
+    assert _q(L, M=1 << 40, K=1 << 20) == EINVAL
+    assert _q(L, ws=None) == EWS
+    assert _q(L, wsb=16) == EWS
+    assert b"workspace" in L.nvfp4_last_error()
+
+
+def _g(L, Aq=FAKE, As=FAKE, Ag=FAKE, Wq=FAKE, Ws=FAKE, Wg=FAKE, bias=None, Cp=FAKE, M=64, N=64,
+       K=64, flags=0):
+    return L.nvfp4_gemm(Aq, As, Ag, Wq, Ws, Wg, bias, Cp, M, N, K, flags, None)
+
+
+def test_gemm_rejects(L):
+    assert _g(L, Aq=None) == EINVAL
+    assert _g(L, Ws=None) == EINVAL
+    assert _g(L, Wg=None) == EINVAL
+    assert _g(L, Cp=None) == EINVAL
+    assert _g(L, Cp=MIS) == EINVAL
+    assert _g(L, Wq=MIS) == EINVAL
+    assert _g(L, bias=MIS) == EINVAL
+    assert _g(L, K=80) == EINVAL
+    assert _g(L, N=0) == EINVAL
+    assert _g(L, M=0) == EINVAL
+    assert _g(L, flags=0x10) == EINVAL
+    assert b"flag" in L.nvfp4_last_error()
+
+
+def test_linear_rejects(L):
+    f = L.nvfp4_linear
+    assert f(None, FAKE, FAKE, FAKE, None, FAKE, 64, 64, 64, 0, FAKE, 1 << 20, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 64, 64, 0, FAKE, 16, None) == EWS
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 64, 64, 0, None, 1 << 20, None) == EWS
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 64, 40, 0, FAKE, 1 << 20, None) == EINVAL
+
+
+def _desc(**kw):
+    d = _lib.KVCacheDesc(100, 24, 128, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 7, 7)
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_kv_init_and_rejects(L):
+    d = _desc()
+    assert L.nvfp4_kv_init(C.byref(d)) == 0
+    assert d.n_tokens == 0 and d.n_chunks == 0
+    assert L.nvfp4_kv_init(None) == EINVAL
+    assert L.nvfp4_kv_init(C.byref(_desc(head_dim=100))) == EINVAL
+    assert L.nvfp4_kv_init(C.byref(_desc(capacity=0))) == EINVAL
+    assert L.nvfp4_kv_init(C.byref(_desc(max_chunks=0))) == EINVAL
+    assert L.nvfp4_kv_init(C.byref(_desc(k_codes=None))) == EINVAL
+    assert L.nvfp4_kv_init(C.byref(_desc(v_scales=MIS))) == EINVAL
+
+
+def test_kv_append_capacity_and_args(L):
+    d = _desc()
+    assert L.nvfp4_kv_init(C.byref(d)) == 0
+    ws, wsb = FAKE, 1 << 20
+    # token capacity
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 101, ws, wsb, None) == ECAP
+    assert d.n_tokens == 0 and d.n_chunks == 0
+    # chunk slots
+    d.n_tokens, d.n_chunks = 10, 4
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, ws, wsb, None) == ECAP
+    assert d.n_tokens == 10 and d.n_chunks == 4
+    d.n_tokens, d.n_chunks = 0, 0
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 0, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), None, FAKE, 1, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, MIS, 1, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, ws, 8, None) == EWS
+    assert L.nvfp4_kv_append(None, FAKE, FAKE, 1, ws, wsb, None) == EINVAL
+    # a corrupted descriptor
+    assert L.nvfp4_kv_append(C.byref(_desc(n_tokens=500)), FAKE, FAKE, 1, ws, wsb, None) == EINVAL
+
+
+def test_kv_dequant_range(L):
+    d = _desc()
+    assert L.nvfp4_kv_init(C.byref(d)) == 0
+    d.n_tokens, d.n_chunks = 20, 1
+    assert L.nvfp4_kv_dequant(C.byref(d), 0, 21, FAKE, FAKE, None) == EINVAL
+    assert L.nvfp4_kv_dequant(C.byref(d), 5, 4, FAKE, FAKE, None) == EINVAL
+    assert L.nvfp4_kv_dequant(C.byref(d), -1, 4, FAKE, FAKE, None) == EINVAL
+    assert L.nvfp4_kv_dequant(C.byref(d), 0, 4, None, FAKE, None) == EINVAL
+    assert L.nvfp4_kv_dequant(C.byref(d), 0, 4, FAKE, MIS, None) == EINVAL
+    # an empty range is a valid no-op that enqueues nothing
+    assert L.nvfp4_kv_dequant(C.byref(d), 3, 3, FAKE, FAKE, None) == 0
+    assert L.nvfp4_kv_dequant(C.byref(d), 3, 3, None, None, None) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        nv.quantize(x)

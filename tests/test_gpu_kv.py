@@ -1,0 +1,107 @@
+"""GPU parity of the NVFP4 KV cache: every append's codes, scales and tensor
+scales bit-exact against the oracle cache, dequant bit-exact against the
+oracle's dequant chain; the full 65536-token workload on sampled chunks."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_amd as nv
+import oracle
+import workloads
+from gpu_helpers import announce, bf16_to_dev, to_bits, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _small_kv(seed, T, H, D):
+    rng = np.random.default_rng(seed)
+    f = rng.uniform(0.5, 4.0, size=H).astype(np.float32)
+    k = rng.standard_normal((T, H, D)).astype(np.float32) * f[None, :, None]
+    v = rng.standard_normal((T, H, D)).astype(np.float32) * f[::-1][None, :, None] * 3
+    return workloads.to_bf16_bits(k), workloads.to_bf16_bits(v)
+
+
+def _compare_cache(gpu, ref, n):
+    assert gpu.n_tokens == ref.n_tokens == n
+    for a, b, name in ((gpu.k_codes, ref.k_codes, "k_codes"), (gpu.v_codes, ref.v_codes, "v_codes"),
+                       (gpu.k_scales, ref.k_scales, "k_scales"), (gpu.v_scales, ref.v_scales, "v_scales")):
+        got = to_np(a)[:n]
+        bad = np.argwhere(got != b[:n])
+        assert bad.size == 0, (name, bad[:5])
+    g = to_np(gpu.gscale)[:gpu.n_chunks]
+    assert np.array_equal(g, np.array(ref.gscale, dtype=np.float32).reshape(-1, 2))
+    assert list(to_np(gpu.chunk_start)[:gpu.n_chunks + 1]) == ref.chunk_start
+
+
+@pytest.mark.parametrize("H,D", [(3, 64), (24, 128), (1, 32)])
+def test_appends_and_dequant_small(H, D):
+    sizes = [5, 1, 17, 8, 3]
+    cap = sum(sizes) + 4
+    gpu = nv.KVCache(cap, H, D, max_chunks=8)
+    ref = oracle.KVCacheRef(cap, H, D)
+    n = 0
+    for i, T in enumerate(sizes):
+        announce(f"kv append H={H} D={D} chunk {i} T={T}")
+        k, v = _small_kv(100 * i + H, T, H, D)
+        gpu.append(bf16_to_dev(k), bf16_to_dev(v))
+        ref.append(k, v)
+        n += T
+        torch.cuda.synchronize()
+        _compare_cache(gpu, ref, n)
+    for t0, t1 in ((0, n), (3, 9), (6, 7), (n - 3, n), (4, 4)):
+        ko, vo = gpu.dequant(t0, t1)
+        torch.cuda.synchronize()
+        rk, rv = ref.dequant(t0, t1)
+        assert np.array_equal(to_bits(ko), rk), (t0, t1)
+        assert np.array_equal(to_bits(vo), rv), (t0, t1)
+
+
+def test_capacity_errors_leave_cache_unchanged():
+    gpu = nv.KVCache(10, 2, 32, max_chunks=2)
+    k, v = _small_kv(1, 6, 2, 32)
+    gpu.append(bf16_to_dev(k), bf16_to_dev(v))
+    with pytest.raises(nv.NVFP4Error) as e:
+        gpu.append(bf16_to_dev(k), bf16_to_dev(v))          # 12 > 10 tokens
+    assert e.value.status == 3 and gpu.n_tokens == 6 and gpu.n_chunks == 1
+    k2, v2 = _small_kv(2, 4, 2, 32)
+    gpu.append(bf16_to_dev(k2), bf16_to_dev(v2))
+    assert gpu.n_tokens == 10 and gpu.n_chunks == 2
+
+
+def test_full_workload_sampled():
+    K, V, sizes = workloads.kv()
+    H, D = workloads.HEADS, workloads.HEAD_DIM
+    T = K.shape[0]
+    announce(f"kv full workload: {len(sizes)} appends, {T} tokens")
+    gpu = nv.KVCache(T, H, D, max_chunks=len(sizes))
+    kd, vd = bf16_to_dev(K), bf16_to_dev(V)
+    starts = np.r_[0, np.cumsum(sizes)]
+    for i, n in enumerate(sizes):
+        gpu.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]])
+    torch.cuda.synchronize()
+    assert gpu.n_tokens == T and gpu.n_chunks == len(sizes)
+    assert list(to_np(gpu.chunk_start)) == list(starts)
+    # bit-exact on sampled chunks (first, a middle one, the 416-token tail)
+    for ci in (0, 37, len(sizes) - 1):
+        a, b = starts[ci], starts[ci + 1]
+        ref = oracle.KVCacheRef(b - a, H, D)
+        ref.append(K[a:b], V[a:b])
+        assert np.array_equal(to_np(gpu.k_codes)[a:b], ref.k_codes)
+        assert np.array_equal(to_np(gpu.v_codes)[a:b], ref.v_codes)
+        assert np.array_equal(to_np(gpu.k_scales)[a:b], ref.k_scales)
+        assert np.array_equal(to_np(gpu.v_scales)[a:b], ref.v_scales)
+        assert tuple(to_np(gpu.gscale)[ci]) == ref.gscale[0]
+        # dequant of the whole cache, sampled on this chunk
+    ko, vo = gpu.dequant(0, T)
+    torch.cuda.synchronize()
+    kb, vb = to_bits(ko), to_bits(vo)
+    for ci in (0, 37, len(sizes) - 1):
+        a, b = starts[ci], starts[ci + 1]
+        ref = oracle.KVCacheRef(b - a, H, D)
+        ref.append(K[a:b], V[a:b])
+        rk, rv = ref.dequant(0, b - a)
+        assert np.array_equal(kb[a:b], rk) and np.array_equal(vb[a:b], rv), ci
+    # storage closed form: 9/8 bytes per element for K and V together
+    nbytes = sum(t.numel() for t in (gpu.k_codes, gpu.v_codes, gpu.k_scales, gpu.v_scales))
+    assert nbytes * 8 == 9 * T * H * D
