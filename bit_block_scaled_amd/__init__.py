@@ -183,16 +183,34 @@ class KVCache:
         return n.value
 
     def append(self, K, V, ws=None):
+        """Append K, V: bf16 [T, heads, head_dim] tensors, or [T, ld] row views
+        (e.g. column slices of a fused QKV output) whose rows hold
+        heads·head_dim contiguous values."""
         T = K.shape[0]
-        shape = (T, self.desc.heads, self.desc.head_dim)
-        _need(K, torch.bfloat16, "K", shape)
-        _need(V, torch.bfloat16, "V", shape)
+        HD = self.desc.heads * self.desc.head_dim
+        for t, name in ((K, "K"), (V, "V")):
+            if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+                raise TypeError(f"{name} must be a bf16 GPU tensor")
+        if K.is_contiguous() and V.is_contiguous():
+            _need(K, torch.bfloat16, "K", (T, self.desc.heads, self.desc.head_dim))
+            _need(V, torch.bfloat16, "V", (T, self.desc.heads, self.desc.head_dim))
+            ld = HD
+        else:
+            if K.dim() != 2 or tuple(K.shape) != (T, HD) or tuple(V.shape) != (T, HD):
+                raise ValueError(f"strided K/V must be 2-D [T, {HD}] row views")
+            if K.stride(1) != 1 or V.stride(1) != 1 or K.stride(0) != V.stride(0):
+                raise ValueError("strided K/V need unit column stride and equal row strides")
+            ld = K.stride(0)
         if ws is None:
             if self._ws is None or self._ws.numel() < self.workspace_bytes(T):
                 self._ws = torch.empty((self.workspace_bytes(T),), dtype=torch.uint8, device=self.device)
             ws = self._ws
-        check(lib().nvfp4_kv_append(C.byref(self.desc), _ptr(K), _ptr(V), T, _ptr(ws), ws.numel(),
+        check(lib().nvfp4_kv_append(C.byref(self.desc), _ptr(K), _ptr(V), T, ld, _ptr(ws), ws.numel(),
                                     _stream(self.device)))
+
+    def reset(self):
+        """Forget every token (host counters only; enqueues nothing)."""
+        check(lib().nvfp4_kv_init(C.byref(self.desc)))
 
     def dequant(self, t0: int, t1: int, k_out=None, v_out=None):
         shape = (t1 - t0, self.desc.heads, self.desc.head_dim)

@@ -49,7 +49,7 @@ _SIGS = {
     "nvfp4_linear": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, C.c_uint32, _p, _sz, _p], C.c_int),
     "nvfp4_kv_init": ([C.POINTER(KVCacheDesc)], C.c_int),
     "nvfp4_kv_append_workspace": ([_i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
-    "nvfp4_kv_append": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _p, _sz, _p], C.c_int),
+    "nvfp4_kv_append": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _i64, _p, _sz, _p], C.c_int),
     "nvfp4_kv_dequant": ([C.POINTER(KVCacheDesc), _i64, _i64, _p, _p, _p], C.c_int),
     "nvfp4_strerror": ([C.c_int], C.c_char_p),
     "nvfp4_last_error": ([], C.c_char_p),

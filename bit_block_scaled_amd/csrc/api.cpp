@@ -25,7 +25,7 @@ bool aligned(const void *p, size_t a = NVFP4_ALIGN) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-constexpr int64_t kMaxElements = int64_t(1) << 40;   // keeps every byte offset in range
+constexpr int64_t kMaxElements = int64_t(1) << 36;   // keeps unit indices below 2^31
 constexpr size_t kQuantWs = size_t(nvfp4::kAmaxBlocks) * sizeof(uint32_t);
 
 int check_mk(int64_t M, int64_t K, const char *who) {
@@ -108,7 +108,7 @@ int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint
   if ((s = check_ptr(gscale, "gscale", 4))) return s;
   if (ws == nullptr || ws_bytes < kQuantWs) return fail(NVFP4_EWORKSPACE, "quantize: workspace too small");
   if ((s = check_ptr(ws, "ws"))) return s;
-  nvfp4::QuantJob j{x, codes, scales, gscale, static_cast<uint32_t *>(ws), M * K};
+  nvfp4::QuantJob j{x, codes, scales, gscale, static_cast<uint32_t *>(ws), M, K, K};
   return hip_status(nvfp4::launch_quantize(&j, 1, static_cast<hipStream_t>(stream)), "quantize");
 }
 
@@ -150,7 +150,7 @@ int nvfp4_linear(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const 
   uint8_t *as = base + w.scales;
   float *ag = reinterpret_cast<float *>(base + w.gscale);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  nvfp4::QuantJob j{x, aq, as, ag, reinterpret_cast<uint32_t *>(base + w.partials), M * K};
+  nvfp4::QuantJob j{x, aq, as, ag, reinterpret_cast<uint32_t *>(base + w.partials), M, K, K};
   if ((s = hip_status(nvfp4::launch_quantize(&j, 1, st), "linear/quantize"))) return s;
   nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, C, M, N, K, flags};
   return hip_status(nvfp4::launch_gemm(a, st), "linear/gemm");
@@ -190,11 +190,13 @@ static int check_cache(const nvfp4_kv_cache *c, const char *who) {
   return NVFP4_OK;
 }
 
-int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T, void *ws,
-                    size_t ws_bytes, void *stream) {
+int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T, int64_t ld,
+                    void *ws, size_t ws_bytes, void *stream) {
   int s;
   if ((s = check_cache(c, "kv_append"))) return s;
   if (T < 1) return fail(NVFP4_EINVAL, "kv_append: T must be >= 1");
+  if (ld < c->heads * c->head_dim || ld % 8) return fail(NVFP4_EINVAL, "kv_append: ld must be >= heads*head_dim and a multiple of 8");
+  if (T > kMaxElements / ld) return fail(NVFP4_EINVAL, "kv_append: T*ld too large");
   if ((s = check_ptr(K, "K"))) return s;
   if ((s = check_ptr(V, "V"))) return s;
   if (T > c->capacity - c->n_tokens) return fail(NVFP4_ECAPACITY, "kv_append: token capacity exceeded");
@@ -205,9 +207,9 @@ int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int
   const int64_t off = c->n_tokens * e;
   uint32_t *parts = static_cast<uint32_t *>(ws);
   nvfp4::QuantJob jobs[2] = {
-      {K, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T * e},
+      {K, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T, e, ld},
       {V, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
-       parts + nvfp4::kAmaxBlocks, T * e}};
+       parts + nvfp4::kAmaxBlocks, T, e, ld}};
   nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
   s = hip_status(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark), "kv_append");
   if (s) return s;

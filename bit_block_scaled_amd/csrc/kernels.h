@@ -9,16 +9,17 @@ namespace nvfp4 {
 // Upper bound on the number of amax partials one quantisation writes.
 constexpr int kAmaxBlocks = 1024;
 
-// One tensor to quantise: `elements` bf16 values (a multiple of 32) from x to
-// codes (elements/2 bytes), scales (elements/16 bytes) and *gscale, using
-// `partials` (kAmaxBlocks uint32) as scratch.
+// One tensor to quantise: `rows` rows of `cols` bf16 values (cols a multiple of
+// 32), row r starting at x + r·ld, into dense codes (rows·cols/2 bytes),
+// scales (rows·cols/16 bytes) and *gscale, using `partials` (kAmaxBlocks
+// uint32) as scratch.  A dense matrix may be passed as one row.
 struct QuantJob {
   const uint16_t *x;
   uint8_t *codes;
   uint8_t *scales;
   float *gscale;
   uint32_t *partials;
-  int64_t elements;
+  int64_t rows, cols, ld;
 };
 
 // KV-cache bookkeeping written by the encode launch of an append:

@@ -12,8 +12,9 @@
 //             g = A/2688; then each thread encodes 32 consecutive elements
 //             (two 16-blocks): block amax → E4M3 scale → reciprocal → E2M1
 //             codes, written as one 16-byte store plus one 2-byte scale store.
-// A flat view suffices: with K % 32 == 0 a 32-element unit never crosses a
-// row, and the row-major code / scale layouts are flat in the same order.
+// With K % 32 == 0 a 32-element unit never crosses a row, and the outputs are
+// dense in unit order; the input may be row-strided (a KV append can read the
+// K and V column slices of a fused QKV output in place).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -23,13 +24,22 @@ constexpr int kThreads = 256;
 
 // One tensor per blockIdx.y (the KV append quantises K and V in one launch).
 struct QuantTensor {
-  const u32x4 *x;        // bf16, 8 per 16-byte chunk
+  const uint16_t *x;     // bf16 input
   uint8_t *codes;        // 16 bytes per 32-element unit
   uint16_t *scales;      // 2 scale bytes per unit
   float *gscale;         // where g is written
   uint32_t *partials;    // kAmaxBlocks partial maxima
   int64_t units;         // elements / 32
+  uint32_t units_per_row;
+  int64_t ld;            // input elements between row starts
 };
+
+// First 16-byte chunk of unit u in the (possibly row-strided) input.
+__device__ __forceinline__ const u32x4 *unit_src(const QuantTensor &T, int64_t u) {
+  const uint32_t row = (uint32_t)u / T.units_per_row;
+  const uint32_t col = (uint32_t)u - row * T.units_per_row;
+  return reinterpret_cast<const u32x4 *>(T.x + (int64_t)row * T.ld + 32 * (int64_t)col);
+}
 struct QuantArgs {
   QuantTensor t[2];
   ChunkMark mark;        // chunk_start == nullptr: nothing to record
@@ -37,28 +47,29 @@ struct QuantArgs {
 
 __global__ void __launch_bounds__(kThreads) k_amax(QuantArgs args) {
   const QuantTensor &T = args.t[blockIdx.y];
-  const int64_t n16 = T.units * 4;                     // uint4 chunks
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t m = 0;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    u32x4 v0 = T.x[i];
-    u32x4 v1 = T.x[i + stride];
-    u32x4 v2 = T.x[i + 2 * stride];
-    u32x4 v3 = T.x[i + 3 * stride];
-    m = absmax_bf16x2(m, v0.x); m = absmax_bf16x2(m, v0.y);
-    m = absmax_bf16x2(m, v0.z); m = absmax_bf16x2(m, v0.w);
-    m = absmax_bf16x2(m, v1.x); m = absmax_bf16x2(m, v1.y);
-    m = absmax_bf16x2(m, v1.z); m = absmax_bf16x2(m, v1.w);
-    m = absmax_bf16x2(m, v2.x); m = absmax_bf16x2(m, v2.y);
-    m = absmax_bf16x2(m, v2.z); m = absmax_bf16x2(m, v2.w);
-    m = absmax_bf16x2(m, v3.x); m = absmax_bf16x2(m, v3.y);
-    m = absmax_bf16x2(m, v3.z); m = absmax_bf16x2(m, v3.w);
+  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; u + stride < T.units; u += 2 * stride) {
+    const u32x4 *p0 = unit_src(T, u), *p1 = unit_src(T, u + stride);
+    const u32x4 a0 = p0[0], a1 = p0[1], a2 = p0[2], a3 = p0[3];
+    const u32x4 b0 = p1[0], b1 = p1[1], b2 = p1[2], b3 = p1[3];
+    m = absmax_bf16x2(m, a0.x); m = absmax_bf16x2(m, a0.y); m = absmax_bf16x2(m, a0.z); m = absmax_bf16x2(m, a0.w);
+    m = absmax_bf16x2(m, a1.x); m = absmax_bf16x2(m, a1.y); m = absmax_bf16x2(m, a1.z); m = absmax_bf16x2(m, a1.w);
+    m = absmax_bf16x2(m, a2.x); m = absmax_bf16x2(m, a2.y); m = absmax_bf16x2(m, a2.z); m = absmax_bf16x2(m, a2.w);
+    m = absmax_bf16x2(m, a3.x); m = absmax_bf16x2(m, a3.y); m = absmax_bf16x2(m, a3.z); m = absmax_bf16x2(m, a3.w);
+    m = absmax_bf16x2(m, b0.x); m = absmax_bf16x2(m, b0.y); m = absmax_bf16x2(m, b0.z); m = absmax_bf16x2(m, b0.w);
+    m = absmax_bf16x2(m, b1.x); m = absmax_bf16x2(m, b1.y); m = absmax_bf16x2(m, b1.z); m = absmax_bf16x2(m, b1.w);
+    m = absmax_bf16x2(m, b2.x); m = absmax_bf16x2(m, b2.y); m = absmax_bf16x2(m, b2.z); m = absmax_bf16x2(m, b2.w);
+    m = absmax_bf16x2(m, b3.x); m = absmax_bf16x2(m, b3.y); m = absmax_bf16x2(m, b3.z); m = absmax_bf16x2(m, b3.w);
   }
-  for (; i < n16; i += stride) {
-    u32x4 v = T.x[i];
-    m = absmax_bf16x2(m, v.x); m = absmax_bf16x2(m, v.y);
-    m = absmax_bf16x2(m, v.z); m = absmax_bf16x2(m, v.w);
+  for (; u < T.units; u += stride) {
+    const u32x4 *p0 = unit_src(T, u);
+    const u32x4 a0 = p0[0], a1 = p0[1], a2 = p0[2], a3 = p0[3];
+    m = absmax_bf16x2(m, a0.x); m = absmax_bf16x2(m, a0.y); m = absmax_bf16x2(m, a0.z); m = absmax_bf16x2(m, a0.w);
+    m = absmax_bf16x2(m, a1.x); m = absmax_bf16x2(m, a1.y); m = absmax_bf16x2(m, a1.z); m = absmax_bf16x2(m, a1.w);
+    m = absmax_bf16x2(m, a2.x); m = absmax_bf16x2(m, a2.y); m = absmax_bf16x2(m, a2.z); m = absmax_bf16x2(m, a2.w);
+    m = absmax_bf16x2(m, a3.x); m = absmax_bf16x2(m, a3.y); m = absmax_bf16x2(m, a3.z); m = absmax_bf16x2(m, a3.w);
   }
   uint32_t mm = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
   mm = wave_max_u32(mm);
@@ -142,7 +153,7 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
   }
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < T.units; u += stride) {
-    const u32x4 *src = T.x + 4 * u;
+    const u32x4 *src = unit_src(T, u);
     const u32x4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
     uint32_t b0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t b1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
@@ -155,7 +166,7 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
 }
 
 static int amax_blocks(int64_t units) {
-  int64_t b = (units * 4 + kThreads * 8 - 1) / (kThreads * 8);   // >= 8 uint4 per thread
+  int64_t b = (units + kThreads * 2 - 1) / (kThreads * 2);        // >= 2 units per thread
   if (b < 1) b = 1;
   if (b > kAmaxBlocks) b = kAmaxBlocks;
   return (int)b;
@@ -174,12 +185,14 @@ hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
   if (mark) a.mark = *mark;
   int64_t max_units = 0;
   for (int i = 0; i < njobs; ++i) {
-    a.t[i].x = reinterpret_cast<const u32x4 *>(jobs[i].x);
+    a.t[i].x = jobs[i].x;
     a.t[i].codes = jobs[i].codes;
     a.t[i].scales = reinterpret_cast<uint16_t *>(jobs[i].scales);
     a.t[i].gscale = jobs[i].gscale;
     a.t[i].partials = jobs[i].partials;
-    a.t[i].units = jobs[i].elements / 32;
+    a.t[i].units = jobs[i].rows * (jobs[i].cols / 32);
+    a.t[i].units_per_row = (uint32_t)(jobs[i].cols / 32);
+    a.t[i].ld = jobs[i].ld;
     if (a.t[i].units > max_units) max_units = a.t[i].units;
   }
   // Both tensors of a pair use the same grid; a tensor with fewer units simply

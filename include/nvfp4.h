@@ -168,13 +168,17 @@ int nvfp4_kv_init(nvfp4_kv_cache *c);
 int nvfp4_kv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t *bytes);
 
 /*
- * Quantise K and V (bf16 [T, heads, head_dim]) into the cache at token offset
- * c->n_tokens, record their tensor scales as chunk c->n_chunks, then advance
- * the counters.  Returns NVFP4_ECAPACITY (cache unchanged) when the tokens or
- * the chunk slots would overflow.  T >= 1.
+ * Quantise K and V (bf16, T tokens of [heads, head_dim]) into the cache at
+ * token offset c->n_tokens, record their tensor scales as chunk c->n_chunks,
+ * then advance the counters.  Returns NVFP4_ECAPACITY (cache unchanged) when
+ * the tokens or the chunk slots would overflow.  T >= 1.
+ *   ld  elements from one token's first element to the next token's, in both
+ *       K and V: heads·head_dim for dense [T, heads, head_dim] tensors, or the
+ *       row length of a fused QKV projection output whose K and V column
+ *       slices are passed directly.  ld >= heads·head_dim, ld % 8 == 0.
  */
 int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T,
-                    void *ws, size_t ws_bytes, void *stream);
+                    int64_t ld, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Dequantise tokens [t0, t1) of K and V to bf16 [t1-t0, heads, head_dim]:

@@ -82,7 +82,7 @@ def test_quantize_rejects(L):
     assert _q(L, K=16) == EINVAL
     assert _q(L, M=0) == EINVAL
     assert _q(L, M=-5) == EINVAL
-    assert _q(L, M=1 << 40, K=1 << 20) == EINVAL
+    assert _q(L, M=1 << 30, K=1 << 10) == EINVAL          # more than 2^36 elements
     assert _q(L, ws=None) == EWS
     assert _q(L, wsb=16) == EWS
     assert b"workspace" in L.nvfp4_last_error()
@@ -140,20 +140,22 @@ def test_kv_append_capacity_and_args(L):
     assert L.nvfp4_kv_init(C.byref(d)) == 0
     ws, wsb = FAKE, 1 << 20
     # token capacity
-    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 101, ws, wsb, None) == ECAP
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 101, 3072, ws, wsb, None) == ECAP
     assert d.n_tokens == 0 and d.n_chunks == 0
     # chunk slots
     d.n_tokens, d.n_chunks = 10, 4
-    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, ws, wsb, None) == ECAP
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, 3072, ws, wsb, None) == ECAP
     assert d.n_tokens == 10 and d.n_chunks == 4
     d.n_tokens, d.n_chunks = 0, 0
-    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 0, ws, wsb, None) == EINVAL
-    assert L.nvfp4_kv_append(C.byref(d), None, FAKE, 1, ws, wsb, None) == EINVAL
-    assert L.nvfp4_kv_append(C.byref(d), FAKE, MIS, 1, ws, wsb, None) == EINVAL
-    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, ws, 8, None) == EWS
-    assert L.nvfp4_kv_append(None, FAKE, FAKE, 1, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 0, 3072, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), None, FAKE, 1, 3072, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, MIS, 1, 3072, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, 3072, ws, 8, None) == EWS
+    assert L.nvfp4_kv_append(None, FAKE, FAKE, 1, 3072, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, 3000, ws, wsb, None) == EINVAL   # ld < H*D
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 1, 3076, ws, wsb, None) == EINVAL   # ld % 8
     # a corrupted descriptor
-    assert L.nvfp4_kv_append(C.byref(_desc(n_tokens=500)), FAKE, FAKE, 1, ws, wsb, None) == EINVAL
+    assert L.nvfp4_kv_append(C.byref(_desc(n_tokens=500)), FAKE, FAKE, 1, 3072, ws, wsb, None) == EINVAL
 
 
 def test_kv_dequant_range(L):

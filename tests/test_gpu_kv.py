@@ -105,3 +105,21 @@ def test_full_workload_sampled():
     # storage closed form: 9/8 bytes per element for K and V together
     nbytes = sum(t.numel() for t in (gpu.k_codes, gpu.v_codes, gpu.k_scales, gpu.v_scales))
     assert nbytes * 8 == 9 * T * H * D
+
+
+def test_strided_append_from_fused_rows():
+    # K and V read in place as column slices of a [T, 3·H·D] row-major matrix
+    # (the layout of a fused QKV projection output), token stride 3·H·D
+    H, D, T = 24, 128, 300
+    rows = workloads.random_matrix(31, T, 3 * H * D, sigma=2.0, outliers=True)
+    dev_rows = bf16_to_dev(rows)
+    gpu = nv.KVCache(T + 10, H, D, max_chunks=2)
+    gpu.append(dev_rows[:, H * D:2 * H * D], dev_rows[:, 2 * H * D:])
+    ref = oracle.KVCacheRef(T + 10, H, D)
+    ref.append(np.ascontiguousarray(rows[:, H * D:2 * H * D]).reshape(T, H, D),
+               np.ascontiguousarray(rows[:, 2 * H * D:]).reshape(T, H, D))
+    torch.cuda.synchronize()
+    _compare_cache(gpu, ref, T)
+    ko, vo = gpu.dequant(0, T)
+    rk, rv = ref.dequant(0, T)
+    assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
