@@ -70,6 +70,7 @@ int check_gemm_args(const uint8_t *Aq, const uint8_t *As, const float *Ag, const
   if ((s = check_mk(M, K, "gemm"))) return s;
   if (N < 1) return fail(NVFP4_EINVAL, "gemm: N must be >= 1");
   if (N > kMaxElements / K || M > kMaxElements / N) return fail(NVFP4_EINVAL, "gemm: problem too large");
+  if (K > (int64_t(1) << 24)) return fail(NVFP4_EINVAL, "gemm: K must be <= 2^24");
   if (flags & ~uint32_t(NVFP4_EPI_GELU_TANH | NVFP4_TILE_MASK))
     return fail(NVFP4_EINVAL, "gemm: unknown flag bits");
   if ((flags & NVFP4_TILE_MASK) > NVFP4_TILE_128x128) return fail(NVFP4_EINVAL, "gemm: unknown tile flag");

@@ -60,6 +60,22 @@ __device__ __forceinline__ uint32_t absmax_bf16x2(uint32_t acc, uint32_t v) {
   return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
 }
 
+// Raw buffer descriptor (stride 0, `bytes` addressable bytes from `base`;
+// loads past the end return 0).  Every field is made wave-uniform so the
+// descriptor lives in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  const uint64_t v = reinterpret_cast<uint64_t>(base);
+  i32x4 d;
+  d.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  d.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(v >> 32) & 0xFFFFu));
+  d.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  d.w = 0x00020000;                        // descriptor word 3 for the gfx9 family
+  __amdgpu_buffer_rsrc_t r;
+  __builtin_memcpy(&r, &d, sizeof(r));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {

@@ -21,16 +21,22 @@
 // The epilogue applies fl32(Ag·Wg), the bias and optional GELU, and rounds to
 // bf16 once.
 //
-// Tiling: 4 waves as 2 x 2; each wave owns (32·WM) activation rows x (32·WN)
-// weight rows and keeps WM·WN 32x32 fp32 accumulators.  K advances in stages of
-// 128 elements (64 code bytes + 8 scale bytes per row) through a
-// double-buffered LDS ring.  Inside a stage each lane reads 16 code bytes of one
-// row (32 consecutive k), i.e. four MFMA fragments; lanes 0-31 and 32-63 take
-// adjacent 32-k halves.  That is a fixed permutation of k applied identically
-// to both operands, which leaves the sum unchanged.  Code chunks sit in LDS
-// chunk-major ([chunk][row][16 B], rows padded by 16) so the 16-byte reads of
-// 32 consecutive rows are contiguous and the row-fastest fills are
-// conflict-free.
+// Tiling: 4 waves as 2 x 2, one wave per SIMD; each wave owns (32·WM)
+// activation rows x (32·WN) weight rows and keeps WM·WN 32x32 fp32 accumulators
+// (AGPRs).  K advances in stages of 128 elements (64 code bytes + 8 scale
+// bytes per row) through two LDS buffers: the workgroup copies stage ks+1 from
+// registers into LDS and fetches stage ks+2 from L2 into registers while it
+// computes stage ks.  Global loads move 64 contiguous bytes of a row per 4
+// lanes (buffer loads; bytes past the tile read as 0); LDS holds codes
+// chunk-major, [chunk][row + 4][16 B], so both the fills and the 16-byte
+// fragment reads of 32 consecutive rows are free of bank conflicts.
+// Lane (r, h) reads chunk 2s + h of row r in sub-step s: k = 64s + 32h + 8t + e
+// for dword t, element e — a fixed permutation of k applied identically to
+// both operands, which leaves the sum unchanged.  Decoding, not data movement,
+// is the scarce resource (the VALU work of the fp16 fragments competes with
+// the MFMAs for issue slots): the decode of step t+1 is issued between the
+// MFMAs of step t (explicit scheduling groups), and the first decode of the
+// next stage overlaps the last MFMAs of the current one.
 #include <nvfp4.h>
 
 #include "device_common.h"
@@ -40,82 +46,6 @@ namespace nvfp4 {
 
 constexpr int kGemmThreads = 256;
 constexpr int kBK = 128;                 // K elements per stage
-constexpr int kChunks = kBK / 32;        // 16-byte code chunks per row per stage
-constexpr int kPadRows = 16;
-
-template <int WM, int WN>
-struct Tile {
-  static constexpr int BM = 64 * WM;
-  static constexpr int BN = 64 * WN;
-  static constexpr int A_CODE = 0;
-  static constexpr int W_CODE = A_CODE + kChunks * (BM + kPadRows) * 16;
-  static constexpr int A_SCALE = W_CODE + kChunks * (BN + kPadRows) * 16;
-  static constexpr int W_SCALE = A_SCALE + BM * 8;
-  static constexpr int STAGE = W_SCALE + BN * 8;
-  static constexpr int LDS = 2 * STAGE;
-};
-
-// ---------------------------------------------------------------------------
-// global → registers → LDS staging of one operand (ROWS rows) for one stage
-
-template <int ROWS>
-struct StageRegs {
-  static constexpr int NC = ROWS * kChunks / kGemmThreads;   // code chunks per thread
-  u32x4 code[NC];
-  u32x2 scale;
-};
-
-template <int ROWS>
-__device__ __forceinline__ void load_stage(StageRegs<ROWS> &s, const uint8_t *codes,
-                                           const uint8_t *scales, int64_t row0, int64_t nrows,
-                                           int64_t K, int ks, bool scale_aligned) {
-  const int t = threadIdx.x;
-  const int64_t row_bytes = K / 2;
-  const int64_t col0 = (int64_t)ks * (kBK / 2);
-#pragma unroll
-  for (int it = 0; it < StageRegs<ROWS>::NC; ++it) {
-    const int q = t + kGemmThreads * it;
-    const int row = q % ROWS, c = q / ROWS;
-    int64_t gr = row0 + row;
-    gr = gr < nrows ? gr : nrows - 1;
-    const int64_t col = col0 + 16 * c;
-    if (col < row_bytes)
-      s.code[it] = *reinterpret_cast<const u32x4 *>(codes + gr * row_bytes + col);
-    else
-      s.code[it] = u32x4{0u, 0u, 0u, 0u};
-  }
-  s.scale = u32x2{0u, 0u};
-  if (t < ROWS) {
-    int64_t gr = row0 + t;
-    gr = gr < nrows ? gr : nrows - 1;
-    const int64_t srow = K / 16;
-    const int64_t scol = (int64_t)ks * (kBK / 16);
-    const uint8_t *p = scales + gr * srow + scol;
-    if (scale_aligned && scol + 8 <= srow) {
-      s.scale = *reinterpret_cast<const u32x2 *>(p);
-    } else {
-      // unaligned row starts or a partial last stage: 2-byte pieces, masked
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (scol + 2 * b + 2 <= srow) w[b] = *reinterpret_cast<const uint16_t *>(p + 2 * b);
-      s.scale = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
-    }
-  }
-}
-
-template <int ROWS>
-__device__ __forceinline__ void store_stage(const StageRegs<ROWS> &s, uint8_t *code_lds,
-                                            uint8_t *scale_lds) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int it = 0; it < StageRegs<ROWS>::NC; ++it) {
-    const int q = t + kGemmThreads * it;
-    const int row = q % ROWS, c = q / ROWS;
-    *reinterpret_cast<u32x4 *>(code_lds + (c * (ROWS + kPadRows) + row) * 16) = s.code[it];
-  }
-  if (t < ROWS) *reinterpret_cast<u32x2 *>(scale_lds + t * 8) = s.scale;
-}
 
 // ---------------------------------------------------------------------------
 // fragment decode: 8 E2M1 codes (one dword) times one E4M3 block scale → f16x8
@@ -147,9 +77,146 @@ __device__ __forceinline__ float gelu_tanh(float y) {
   return y / (1.0f + __expf(-2.0f * z));
 }
 
+constexpr int kChunks = kBK / 32;        // 16-byte code chunks per row per stage
+constexpr int kPadRows = 4;              // LDS row padding per chunk column
+
 template <int WM, int WN>
+struct Tile {
+  static constexpr int BM = 64 * WM, BN = 64 * WN;
+  static constexpr int A_CODE = 0;
+  static constexpr int W_CODE = A_CODE + kChunks * (BM + kPadRows) * 16;
+  static constexpr int A_SCALE = W_CODE + kChunks * (BN + kPadRows) * 16;
+  static constexpr int W_SCALE = A_SCALE + BM * 8;
+  static constexpr int STAGE = W_SCALE + BN * 8;
+  static constexpr int LDS = 2 * STAGE;
+};
+
+struct Operand {
+  const uint8_t *codes;     // first row of the tile
+  const uint8_t *scales;
+  uint32_t code_bytes;      // bytes of the tile's rows (loads beyond read 0)
+  uint32_t scale_bytes;
+};
+
+// One operand's share of a stage in flight in registers: ROWS·4 code chunks
+// over 256 threads (4 lanes per row, 64 contiguous bytes), 8 scale bytes for
+// the first ROWS threads.
+template <int ROWS>
+struct Fill {
+  static constexpr int NC = ROWS * kChunks / kGemmThreads;
+  u32x4 code[NC];
+  u32x2 scale;
+};
+
+template <int ROWS, bool KTAIL>
+__device__ __forceinline__ void fill_load(Fill<ROWS> &f, const Operand &op, int64_t K, int ks) {
+  const int t = threadIdx.x;
+  const uint32_t rb = (uint32_t)(K / 2), sb = (uint32_t)(K / 16);
+  const uint32_t coff = (uint32_t)ks * (kBK / 2), soff = (uint32_t)ks * (kBK / 16);
+  const uint32_t cn = op.code_bytes > coff ? op.code_bytes - coff : 0u;
+  const uint32_t sn = op.scale_bytes > soff ? op.scale_bytes - soff : 0u;
+  const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(op.codes + coff, cn);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(op.scales + soff, sn);
+#pragma unroll
+  for (int it = 0; it < Fill<ROWS>::NC; ++it) {
+    const int q = t + kGemmThreads * it;
+    const int row = q >> 2, c = q & 3;
+    f.code[it] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(row * rb + 16 * c), 0, 0);
+    if (KTAIL && coff + 16 * c >= rb) f.code[it] = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (t < ROWS) {
+    if (!KTAIL) {
+      f.scale = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(t * sb), 0, 0);
+    } else {   // scale rows only 2-byte aligned, last stage partial
+      uint32_t w[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        w[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(t * sb + 2 * b), 0, 0);
+        if (soff + 2 * b >= sb) w[b] = 0u;
+      }
+      f.scale = u32x2{(w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16)};
+    }
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void fill_store(const Fill<ROWS> &f, uint8_t *code_lds, uint8_t *scale_lds) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < Fill<ROWS>::NC; ++it) {
+    const int q = t + kGemmThreads * it;
+    const int row = q >> 2, c = q & 3;
+    *reinterpret_cast<u32x4 *>(code_lds + (c * (ROWS + kPadRows) + row) * 16) = f.code[it];
+  }
+  if (t < ROWS) *reinterpret_cast<u32x2 *>(scale_lds + t * 8) = f.scale;
+}
+
+// A wave's view of one stage: codes of both sub-steps and the 8 scale bytes,
+// per row block q (A blocks first, then W blocks).
+template <int NQ>
+struct Frag {
+  u32x4 c[2][NQ];
+  u32x2 sc[NQ];
+};
+
+template <int WM, int WN>
+__device__ __forceinline__ void frag_read(Frag<WM + WN> &fr, const uint8_t *buf, int wm, int wn,
+                                          int r, int h) {
+  using T = Tile<WM, WN>;
+#pragma unroll
+  for (int i = 0; i < WM; ++i) {
+    const int row = wm * 32 * WM + 32 * i + r;
+    fr.sc[i] = *reinterpret_cast<const u32x2 *>(buf + T::A_SCALE + row * 8);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      fr.c[s][i] = *reinterpret_cast<const u32x4 *>(buf + T::A_CODE + ((2 * s + h) * (T::BM + kPadRows) + row) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < WN; ++j) {
+    const int row = wn * 32 * WN + 32 * j + r;
+    fr.sc[WM + j] = *reinterpret_cast<const u32x2 *>(buf + T::W_SCALE + row * 8);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      fr.c[s][WM + j] = *reinterpret_cast<const u32x4 *>(buf + T::W_CODE + ((2 * s + h) * (T::BN + kPadRows) + row) * 16);
+  }
+}
+
+// Decode step T (0..7) of a stage into fragments f: dword T%4 of sub-step T/4,
+// block 4·(T/4) + 2h + (T%4)/2 of the stage → byte (T%4)/2 of the lane's pair.
+template <int T, int NQ>
+__device__ __forceinline__ void decode_step(const Frag<NQ> &fr, int h, f16x8 (&f)[NQ]) {
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const uint32_t pair = (T < 4 ? fr.sc[q].x : fr.sc[q].y) >> (16 * h);
+    const uint32_t sp = scale_pair_f16(pair >> (8 * ((T & 3) >> 1)));
+    f[q] = decode8(fr.c[T >> 2][q][T & 3], sp);
+  }
+}
+
+template <int WM, int WN>
+__device__ __forceinline__ void mfma_step(f32x16 (&acc)[WN][WM], const f16x8 (&f)[WM + WN]) {
+#pragma unroll
+  for (int j = 0; j < WN; ++j)
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+      acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[WM + j], f[i], acc[j][i], 0, 0, 0);
+}
+
+// Scheduling groups for one step: one MFMA, then up to VPM VALU ops, repeated.
+template <int WM, int WN>
+__device__ __forceinline__ void interleave_hint() {
+  constexpr int VPM = (9 * (WM + WN) + WM * WN - 1) / (WM * WN);
+#pragma unroll
+  for (int k = 0; k < WM * WN; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+  }
+}
+
+template <int WM, int WN, bool KTAIL>
 __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_m, int tiles_n) {
   using T = Tile<WM, WN>;
+  constexpr int BM = T::BM, BN = T::BN, NQ = WM + WN;
   __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
 
   // tile order: contiguous runs of tiles per XCD (workgroups are dealt to the
@@ -165,12 +232,19 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
   const int in = b - grp * per_group;
   const int tile_m = first_m + in % gsz, tile_n = in / gsz;
 
-  const int64_t m0 = (int64_t)tile_m * T::BM, n0 = (int64_t)tile_n * T::BN;
+  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int r = lane & 31, h = lane >> 5;
   const int nk = (int)((a.K + kBK - 1) / kBK);
-  const bool scale_aligned = (a.K % kBK) == 0;
+  const int64_t rb = a.K / 2, sbytes = a.K / 16;
+
+  // rows past the matrix end are outside the buffer ranges and read as 0;
+  // their results are not stored
+  const int64_t rows_a = (a.M - m0) < BM ? (a.M - m0) : BM;
+  const int64_t rows_w = (a.N - n0) < BN ? (a.N - n0) : BN;
+  const Operand opa{a.Aq + m0 * rb, a.As + m0 * sbytes, (uint32_t)(rows_a * rb), (uint32_t)(rows_a * sbytes)};
+  const Operand opw{a.Wq + n0 * rb, a.Ws + n0 * sbytes, (uint32_t)(rows_w * rb), (uint32_t)(rows_w * sbytes)};
 
   f32x16 acc[WN][WM];
 #pragma unroll
@@ -180,72 +254,43 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
 
-  StageRegs<T::BM> ra;
-  StageRegs<T::BN> rw;
-  load_stage<T::BM>(ra, a.Aq, a.As, m0, a.M, a.K, 0, scale_aligned);
-  load_stage<T::BN>(rw, a.Wq, a.Ws, n0, a.N, a.K, 0, scale_aligned);
-  store_stage<T::BM>(ra, smem + T::A_CODE, smem + T::A_SCALE);
-  store_stage<T::BN>(rw, smem + T::W_CODE, smem + T::W_SCALE);
+  Fill<BM> fa;
+  Fill<BN> fw;
+  // prologue: stage 0 into LDS buffer 0, stage 1 in flight in registers
+  fill_load<BM, KTAIL>(fa, opa, a.K, 0);
+  fill_load<BN, KTAIL>(fw, opw, a.K, 0);
+  fill_store<BM>(fa, smem + T::A_CODE, smem + T::A_SCALE);
+  fill_store<BN>(fw, smem + T::W_CODE, smem + T::W_SCALE);
+  fill_load<BM, KTAIL>(fa, opa, a.K, 1);
+  fill_load<BN, KTAIL>(fw, opw, a.K, 1);
   __syncthreads();
 
+  Frag<NQ> fr;
+  f16x8 f0[NQ], f1[NQ];
+  frag_read<WM, WN>(fr, smem, wm, wn, r, h);
+  decode_step<0, NQ>(fr, h, f0);
+
   for (int ks = 0; ks < nk; ++ks) {
-    uint8_t *cur = smem + (ks & 1) * T::STAGE;
     uint8_t *nxt = smem + ((ks + 1) & 1) * T::STAGE;
-    const bool more = ks + 1 < nk;
-    if (more) {
-      load_stage<T::BM>(ra, a.Aq, a.As, m0, a.M, a.K, ks + 1, scale_aligned);
-      load_stage<T::BN>(rw, a.Wq, a.Ws, n0, a.N, a.K, ks + 1, scale_aligned);
-    }
+    // stage ks+1 (in registers) → LDS; fetch stage ks+2.  The buffer being
+    // overwritten was last read at the start of stage ks-1, before the
+    // barrier that ended it.
+    fill_store<BM>(fa, nxt + T::A_CODE, nxt + T::A_SCALE);
+    fill_store<BN>(fw, nxt + T::W_CODE, nxt + T::W_SCALE);
+    fill_load<BM, KTAIL>(fa, opa, a.K, ks + 2);
+    fill_load<BN, KTAIL>(fw, opw, a.K, ks + 2);
 
-    u32x2 sa[WM], sw[WN];
-#pragma unroll
-    for (int i = 0; i < WM; ++i)
-      sa[i] = *reinterpret_cast<const u32x2 *>(cur + T::A_SCALE + (wm * 32 * WM + 32 * i + r) * 8);
-#pragma unroll
-    for (int j = 0; j < WN; ++j)
-      sw[j] = *reinterpret_cast<const u32x2 *>(cur + T::W_SCALE + (wn * 32 * WN + 32 * j + r) * 8);
-
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int c = 2 * s + h;
-      u32x4 qa[WM], qw[WN];
-      uint32_t sca[WM][2], scw[WN][2];
-#pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        qa[i] = *reinterpret_cast<const u32x4 *>(
-            cur + T::A_CODE + (c * (T::BM + kPadRows) + wm * 32 * WM + 32 * i + r) * 16);
-        const uint32_t p = (s ? sa[i].y : sa[i].x) >> (16 * h);
-        sca[i][0] = scale_pair_f16(p);
-        sca[i][1] = scale_pair_f16(p >> 8);
-      }
-#pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        qw[j] = *reinterpret_cast<const u32x4 *>(
-            cur + T::W_CODE + (c * (T::BN + kPadRows) + wn * 32 * WN + 32 * j + r) * 16);
-        const uint32_t p = (s ? sw[j].y : sw[j].x) >> (16 * h);
-        scw[j][0] = scale_pair_f16(p);
-        scw[j][1] = scale_pair_f16(p >> 8);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f16x8 fa[WM], fw[WN];
-#pragma unroll
-        for (int i = 0; i < WM; ++i) fa[i] = decode8(qa[i][t], sca[i][t >> 1]);
-#pragma unroll
-        for (int j = 0; j < WN; ++j) fw[j] = decode8(qw[j][t], scw[j][t >> 1]);
-#pragma unroll
-        for (int j = 0; j < WN; ++j)
-#pragma unroll
-          for (int i = 0; i < WM; ++i)
-            acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fw[j], fa[i], acc[j][i], 0, 0, 0);
-      }
-    }
-
-    if (more) {
-      store_stage<T::BM>(ra, nxt + T::A_CODE, nxt + T::A_SCALE);
-      store_stage<T::BN>(rw, nxt + T::W_CODE, nxt + T::W_SCALE);
-    }
+    decode_step<1, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
+    decode_step<2, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
+    decode_step<3, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
+    decode_step<4, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
+    decode_step<5, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
+    decode_step<6, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
+    decode_step<7, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
+    // every wave has stored stage ks+1 and finished reading stage ks
     __syncthreads();
+    frag_read<WM, WN>(fr, nxt, wm, wn, r, h);
+    decode_step<0, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
   }
 
   // ---- epilogue: acc[j][i][v] is C[m][n] with m = (row block i) + r,
@@ -329,9 +374,12 @@ void gemm_tile_for(int64_t M, int64_t N, int64_t, int *bm, int *bn) {
 
 template <int WM, int WN>
 static hipError_t launch_t(const GemmArgs &a, hipStream_t stream) {
-  using T = Tile<WM, WN>;
-  const int tm = (int)((a.M + T::BM - 1) / T::BM), tn = (int)((a.N + T::BN - 1) / T::BN);
-  hipLaunchKernelGGL((k_gemm<WM, WN>), dim3(tm * tn), dim3(kGemmThreads), 0, stream, a, tm, tn);
+  constexpr int BM = 64 * WM, BN = 64 * WN;
+  const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
+  if (a.K % kBK == 0)
+    hipLaunchKernelGGL((k_gemm<WM, WN, false>), dim3(tm * tn), dim3(kGemmThreads), 0, stream, a, tm, tn);
+  else
+    hipLaunchKernelGGL((k_gemm<WM, WN, true>), dim3(tm * tn), dim3(kGemmThreads), 0, stream, a, tm, tn);
   return hipGetLastError();
 }
 
