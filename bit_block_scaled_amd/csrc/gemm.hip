@@ -121,21 +121,22 @@ __device__ __forceinline__ void fill_load(Fill<ROWS> &f, const Operand &op, int6
   for (int it = 0; it < Fill<ROWS>::NC; ++it) {
     const int q = t + kGemmThreads * it;
     const int row = q >> 2, c = q & 3;
-    f.code[it] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(row * rb + 16 * c), 0, 0);
-    if (KTAIL && coff + 16 * c >= rb) f.code[it] = u32x4{0u, 0u, 0u, 0u};
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(row * rb + 16 * c), 0, 0);
+    f.code[it] = (KTAIL && coff + 16 * c >= rb) ? u32x4{0u, 0u, 0u, 0u} : v;
   }
-  if (t < ROWS) {
-    if (!KTAIL) {
-      f.scale = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(t * sb), 0, 0);
-    } else {   // scale rows only 2-byte aligned, last stage partial
-      uint32_t w[4];
+  // threads past the last row reload (and later re-store) the last row: no
+  // divergent branch in the main loop
+  const int srow = t < ROWS ? t : ROWS - 1;
+  if (!KTAIL) {
+    f.scale = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)(srow * sb), 0, 0);
+  } else {   // scale rows only 2-byte aligned, last stage partial
+    uint32_t w[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        w[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(t * sb + 2 * b), 0, 0);
-        if (soff + 2 * b >= sb) w[b] = 0u;
-      }
-      f.scale = u32x2{(w[0] & 0xFFFFu) | (w[1] << 16), (w[2] & 0xFFFFu) | (w[3] << 16)};
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t v = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(srow * sb + 2 * b), 0, 0);
+      w[b] = (soff + 2 * b >= sb) ? 0u : (v & 0xFFFFu);
     }
+    f.scale = u32x2{w[0] | (w[1] << 16), w[2] | (w[3] << 16)};
   }
 }
 
@@ -148,7 +149,8 @@ __device__ __forceinline__ void fill_store(const Fill<ROWS> &f, uint8_t *code_ld
     const int row = q >> 2, c = q & 3;
     *reinterpret_cast<u32x4 *>(code_lds + (c * (ROWS + kPadRows) + row) * 16) = f.code[it];
   }
-  if (t < ROWS) *reinterpret_cast<u32x2 *>(scale_lds + t * 8) = f.scale;
+  const int srow = t < ROWS ? t : ROWS - 1;
+  *reinterpret_cast<u32x2 *>(scale_lds + srow * 8) = f.scale;
 }
 
 // A wave's view of one stage: codes of both sub-steps and the 8 scale bytes,
@@ -202,14 +204,19 @@ __device__ __forceinline__ void mfma_step(f32x16 (&acc)[WN][WM], const f16x8 (&f
       acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f[WM + j], f[i], acc[j][i], 0, 0, 0);
 }
 
-// Scheduling groups for one step: one MFMA, then up to VPM VALU ops, repeated.
-template <int WM, int WN>
+// Scheduling groups for one step: one MFMA, then up to VPM VALU ops, repeated;
+// in step 0 each of the first MFMAs also takes one LDS store of the fill, in
+// step 1 one global load of the next fill.
+template <int WM, int WN, int STEP>
 __device__ __forceinline__ void interleave_hint() {
   constexpr int VPM = (9 * (WM + WN) + WM * WN - 1) / (WM * WN);
+  constexpr int NFILL = WM + WN + 2;          // fill instructions per thread of each kind
 #pragma unroll
   for (int k = 0; k < WM * WN; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+    if (STEP == 0 && k < NFILL) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    if (STEP == 1 && k < NFILL) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   }
 }
 
@@ -280,62 +287,93 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
     fill_load<BM, KTAIL>(fa, opa, a.K, ks + 2);
     fill_load<BN, KTAIL>(fw, opw, a.K, ks + 2);
 
-    decode_step<1, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
-    decode_step<2, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
-    decode_step<3, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
-    decode_step<4, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
-    decode_step<5, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
-    decode_step<6, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
-    decode_step<7, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN>();
+    decode_step<1, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN, 0>();
+    decode_step<2, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN, 1>();
+    decode_step<3, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN, 2>();
+    decode_step<4, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN, 3>();
+    decode_step<5, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN, 4>();
+    decode_step<6, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN, 5>();
+    decode_step<7, NQ>(fr, h, f1); mfma_step<WM, WN>(acc, f0); interleave_hint<WM, WN, 6>();
     // every wave has stored stage ks+1 and finished reading stage ks
     __syncthreads();
     frag_read<WM, WN>(fr, nxt, wm, wn, r, h);
-    decode_step<0, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN>();
+    decode_step<0, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN, 7>();
   }
 
   // ---- epilogue: acc[j][i][v] is C[m][n] with m = (row block i) + r,
-  //      n = (column block j) + 8·(v/4) + 4·h + v%4.  Each operation rounds
-  //      on its own (no fused multiply-add), as the interface states.
+  //      n = (column block j) + 8·(v/4) + 4·h + v%4.  Each operation rounds on
+  //      its own (no fused multiply-add), as the interface states.  Each row
+  //      block is staged through the wave's own LDS region so the stores are
+  //      16 contiguous bytes per lane along the rows of C.
+  __syncthreads();                       // every wave is done with the stage buffers
   {
 #pragma clang fp contract(off)
-  const float gg = a.Ag[0] * a.Wg[0];
-  const bool gelu = (a.flags & NVFP4_EPI_GELU_TANH) != 0;
-  const bool vec_ok = (a.N & 3) == 0;
+    constexpr int PITCH = 64 * WN + 16;  // bytes per staged row (32·WN bf16 + pad)
+    constexpr int CPR = 4 * WN;          // 16-byte chunks per staged row
+    uint8_t *wreg = smem + wave * 32 * PITCH;
+    const int64_t mw = m0 + wm * 32 * WM, nw = n0 + wn * 32 * WN;
+    const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N) && ((a.N & 7) == 0);
+    const float gg = a.Ag[0] * a.Wg[0];
+    const bool gelu = (a.flags & NVFP4_EPI_GELU_TANH) != 0;
+    const bool has_bias = a.bias != nullptr;
+
+    float bv[WN][4][4];
 #pragma unroll
-  for (int j = 0; j < WN; ++j) {
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n = n0 + wn * 32 * WN + 32 * j + 8 * q + 4 * h;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (a.bias) {
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = nw + 32 * j + 8 * q + 4 * h;
+        if (has_bias && full) {
+          const u32x2 p = *reinterpret_cast<const u32x2 *>(a.bias + n);
+          bv[j][q][0] = bf16_bits_to_f32(p.x & 0xFFFFu);
+          bv[j][q][1] = bf16_bits_to_f32(p.x >> 16);
+          bv[j][q][2] = bf16_bits_to_f32(p.y & 0xFFFFu);
+          bv[j][q][3] = bf16_bits_to_f32(p.y >> 16);
+        } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (n + k < a.N) bv[k] = bf16_bits_to_f32(a.bias[n + k]);
-      }
-#pragma unroll
-      for (int i = 0; i < WM; ++i) {
-        const int64_t m = m0 + wm * 32 * WM + 32 * i + r;
-        float o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float y = acc[j][i][4 * q + k] * gg;
-          if (a.bias) y = y + bv[k];
-          if (gelu) y = gelu_tanh(y);
-          o[k] = y;
+          for (int k = 0; k < 4; ++k)
+            bv[j][q][k] = (has_bias && n + k < a.N) ? bf16_bits_to_f32(a.bias[n + k]) : 0.0f;
         }
-        if (m < a.M) {
-          uint16_t *dst = a.C + m * a.N + n;
-          if (vec_ok && n + 3 < a.N) {
-            *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-          } else {
+      }
+
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-              if (n + k < a.N) dst[k] = (uint16_t)(pack_bf16x2(o[k], 0.0f) & 0xFFFFu);
+    for (int i = 0; i < WM; ++i) {
+#pragma unroll
+      for (int j = 0; j < WN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float o[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float y = acc[j][i][4 * q + k] * gg;
+            if (has_bias) y = y + bv[j][q][k];
+            if (gelu) y = gelu_tanh(y);
+            o[k] = y;
+          }
+          *reinterpret_cast<u32x2 *>(wreg + r * PITCH + (32 * j + 8 * q + 4 * h) * 2) =
+              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
+#pragma unroll
+      for (int it = 0; it < 2 * WN; ++it) {
+        const int g = it * 64 + lane;
+        const int row = g / CPR, c = g % CPR;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(wreg + row * PITCH + 16 * c);
+        const int64_t m = mw + 32 * i + row, n = nw + 8 * c;
+        uint16_t *dst = a.C + m * a.N + n;
+        if (full) {
+          *reinterpret_cast<u32x4 *>(dst) = v;
+        } else if (m < a.M) {
+          if ((a.N & 7) == 0 && n + 8 <= a.N) {
+            *reinterpret_cast<u32x4 *>(dst) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < a.N) dst[e] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
           }
         }
       }
     }
-  }
   }
 }
 
