@@ -26,7 +26,7 @@ bool aligned(const void *p, size_t a = NVFP4_ALIGN) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int64_t kMaxElements = int64_t(1) << 36;   // keeps unit indices below 2^31
-constexpr size_t kQuantWs = size_t(nvfp4::kAmaxBlocks) * sizeof(uint32_t);
+constexpr size_t kQuantWs = nvfp4::kQuantScratchBytes;
 
 int check_mk(int64_t M, int64_t K, const char *who) {
   if (M < 1) return fail(NVFP4_EINVAL, std::string(who) + ": M must be >= 1");
@@ -210,7 +210,7 @@ int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int
   nvfp4::QuantJob jobs[2] = {
       {K, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T, e, ld},
       {V, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
-       parts + nvfp4::kAmaxBlocks, T, e, ld}};
+       parts + kQuantWs / sizeof(uint32_t), T, e, ld}};
   nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
   s = hip_status(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark), "kv_append");
   if (s) return s;

@@ -6,13 +6,18 @@
 
 namespace nvfp4 {
 
-// Upper bound on the number of amax partials one quantisation writes.
+// Upper bound on the number of amax partials a two-pass quantisation writes.
 constexpr int kAmaxBlocks = 1024;
+// Slots of a resident (single-pass) quantisation: one 64-bit word per
+// workgroup plus the published result at index kResidentSlots.
+constexpr int kResidentSlots = 4096;
+// Scratch bytes per quantised tensor (covers both uses; a multiple of 256).
+constexpr size_t kQuantScratchBytes = 8 * (size_t(kResidentSlots) + 32);
 
 // One tensor to quantise: `rows` rows of `cols` bf16 values (cols a multiple of
 // 32), row r starting at x + r·ld, into dense codes (rows·cols/2 bytes),
-// scales (rows·cols/16 bytes) and *gscale, using `partials` (kAmaxBlocks
-// uint32) as scratch.  A dense matrix may be passed as one row.
+// scales (rows·cols/16 bytes) and *gscale, using `partials`
+// (kQuantScratchBytes, 8-byte aligned) as scratch.  A dense matrix may be passed as one row.
 struct QuantJob {
   const uint16_t *x;
   uint8_t *codes;
@@ -30,7 +35,8 @@ struct ChunkMark {
   int64_t value;
 };
 
-// Quantises one or two tensors (njobs in {1, 2}) with two launches on `stream`.
+// Quantises one or two tensors (njobs in {1, 2}) on `stream`: one launch when
+// the grid fits on the device at once, else two launches.
 hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
                            const ChunkMark *mark = nullptr);
 

@@ -4,19 +4,26 @@
 // KV cache is stored quantised per chunk and read back through a dequant
 // kernel; 二、方法 / NVFP4 量化格式: Dequant = X^FP4 · α^FP8 · α^FP32.
 //
-// Each thread turns 32 consecutive elements (16 code bytes, 2 scale bytes) of
-// one tensor into 64 bytes of bf16:  out = bf16(fl32(fl32(E2M1·S)·g)), where g
-// is the tensor scale of the append that wrote the token (binary search over
-// the chunk start offsets).  The E2M1·S product is exact in binary32.
+// Layout of the work: every lane turns one 8-element chunk (4 code bytes, one
+// scale byte shared with its neighbour lane) into 16 bytes of bf16, so each
+// load and store instruction of a wave covers consecutive memory; a workgroup
+// handles kKvU chunks per lane.  out = bf16(fl32(fl32(E2M1·S)·g)), where g is
+// the tensor scale of the append that wrote the token, found by binary search
+// over the chunk start offsets (copied to LDS when they fit).  The E2M1·S
+// product is exact in binary32.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nvfp4 {
 
 constexpr int kKvThreads = 256;
+constexpr int kKvU = 4;                    // chunks per lane
+constexpr int kKvLdsStarts = 2048;         // chunk starts held in LDS
 
-__device__ __forceinline__ int64_t chunk_of(const int64_t *starts, int64_t n_chunks, int64_t t) {
-  int64_t lo = 0, hi = n_chunks - 1;      // invariant: starts[lo] <= t < starts[hi + 1]
+// Index of the chunk holding token t: starts[lo] <= t < starts[lo + 1].
+template <typename P>
+__device__ __forceinline__ int64_t chunk_of(P starts, int64_t n_chunks, int64_t t) {
+  int64_t lo = 0, hi = n_chunks - 1;
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) >> 1;
     if (starts[mid] <= t) lo = mid; else hi = mid - 1;
@@ -24,8 +31,8 @@ __device__ __forceinline__ int64_t chunk_of(const int64_t *starts, int64_t n_chu
   return lo;
 }
 
-// Two bf16 from the 2 codes of byte SEL of `w`: (E2M1 · s) · g, rounded once
-// to binary32 and once to bf16.
+// Eight bf16 from the 8 codes of `w`: (E2M1 · s) · g, rounded once to
+// binary32 and once to bf16.
 template <int SEL>
 __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, float s, float g) {
   const f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
@@ -43,31 +50,45 @@ __device__ __forceinline__ u32x4 dequant_dword(uint32_t w, float s, float g) {
 
 __global__ void __launch_bounds__(kKvThreads) k_kv_dequant(KvDequantArgs a) {
   const int which = blockIdx.y;
-  const int64_t units_per_token = a.elems_per_token / 32;
-  const int64_t base_unit = a.t0 * units_per_token;
-  const int64_t units = (a.t1 - a.t0) * units_per_token;
-  const u32x4 *codes = reinterpret_cast<const u32x4 *>(a.codes[which]) + base_unit;
-  const uint16_t *scales = reinterpret_cast<const uint16_t *>(a.scales[which]) + base_unit;
+  const int64_t e = a.elems_per_token;
+  const int64_t base = a.t0 * e / 8;                 // first chunk of the range
+  const int64_t chunks = (a.t1 - a.t0) * e / 8;
+  const uint32_t *codes = reinterpret_cast<const uint32_t *>(a.codes[which]) + base;
+  const uint8_t *scales = a.scales[which] + base / 2;
   u32x4 *out = reinterpret_cast<u32x4 *>(a.out[which]);
-  const int64_t stride = (int64_t)gridDim.x * kKvThreads;
-  for (int64_t u = (int64_t)blockIdx.x * kKvThreads + threadIdx.x; u < units; u += stride) {
-    const int64_t t = a.t0 + u / units_per_token;
-    const float g = a.gscale[2 * chunk_of(a.chunk_start, a.n_chunks, t) + which];
-    const u32x4 c = codes[u];
-    const uint32_t sb = scales[u];
-    const float s0 = e4m3_decode(sb & 0xFFu), s1 = e4m3_decode(sb >> 8);
-    out[4 * u + 0] = dequant_dword(c.x, s0, g);
-    out[4 * u + 1] = dequant_dword(c.y, s0, g);
-    out[4 * u + 2] = dequant_dword(c.z, s1, g);
-    out[4 * u + 3] = dequant_dword(c.w, s1, g);
+  const bool narrow = 8 * (chunks + kKvThreads * kKvU) < (int64_t(1) << 32);   // 32-bit token division
+
+  // loads first, so the chunk search below overlaps them
+  uint32_t c[kKvU], sb[kKvU];
+#pragma unroll
+  for (int i = 0; i < kKvU; ++i) {
+    const int64_t q = ((int64_t)blockIdx.x * kKvU + i) * kKvThreads + threadIdx.x;
+    c[i] = q < chunks ? codes[q] : 0u;
+    sb[i] = q < chunks ? scales[q >> 1] : 0u;
+  }
+  __shared__ int64_t st[kKvLdsStarts];
+  const bool in_lds = a.n_chunks < kKvLdsStarts;
+  if (in_lds) {
+    for (int64_t j = threadIdx.x; j <= a.n_chunks; j += kKvThreads) st[j] = a.chunk_start[j];
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < kKvU; ++i) {
+    const int64_t q = ((int64_t)blockIdx.x * kKvU + i) * kKvThreads + threadIdx.x;
+    const int64_t t = a.t0 + (narrow ? (int64_t)((uint32_t)(8 * q) / (uint32_t)e) : (8 * q) / e);
+    const int64_t ci = in_lds ? chunk_of(st, a.n_chunks, t) : chunk_of(a.chunk_start, a.n_chunks, t);
+    const float g = a.gscale[2 * ci + which];
+    const u32x4 o = dequant_dword(c[i], e4m3_decode(sb[i]), g);
+    if (q < chunks) out[q] = o;
   }
 }
 
 hipError_t launch_kv_dequant(const KvDequantArgs &a, hipStream_t stream) {
-  const int64_t units = (a.t1 - a.t0) * (a.elems_per_token / 32);
-  if (units <= 0) return hipSuccess;
-  int64_t blocks = (units + kKvThreads - 1) / kKvThreads;
-  if (blocks > 8192) blocks = 8192;
+  const int64_t chunks = (a.t1 - a.t0) * (a.elems_per_token / 8);
+  if (chunks <= 0) return hipSuccess;
+  const int64_t per_block = (int64_t)kKvThreads * kKvU;
+  const int64_t blocks = (chunks + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_kv_dequant, dim3((unsigned)blocks, 2), dim3(kKvThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -5,16 +5,31 @@
 // NVFP4 训练的工程细节 (1-D block scaling of activations).  The same kernels
 // quantise the KV cache in place (二、方法 / 推理底座).
 //
-// Two passes over the input:
-//   k_amax    grid-stride max of |x| (on the 15-bit magnitude pattern, which
-//             orders like the value for finite bf16); one partial per block.
-//   k_encode  every block first folds the partials into A and derives
-//             g = A/2688; then each thread encodes 32 consecutive elements
-//             (two 16-blocks): block amax → E4M3 scale → reciprocal → E2M1
-//             codes, written as one 16-byte store plus one 2-byte scale store.
-// With K % 32 == 0 a 32-element unit never crosses a row, and the outputs are
-// dense in unit order; the input may be row-strided (a KV append can read the
-// K and V column slices of a fused QKV output in place).
+// Two implementations of the same arithmetic:
+//
+//   resident (one launch, the input is read once)
+//             every lane loads whole 16-element blocks (32 bytes each) and
+//             keeps them in registers; each workgroup publishes its |x| maximum
+//             in a 64-bit (call epoch, amax) slot; workgroup 0 folds the slots
+//             and publishes A the same way; every workgroup then encodes its
+//             registers, one 8-byte code store and one scale byte per block.
+//             Used whenever the whole grid fits on the device at once; a
+//             workgroup whose wait for A expires computes A from the whole
+//             input itself, so the result does not depend on residency.
+//   two-pass  k_amax (grid-stride max of |x|, one partial per block), then
+//             k_encode (every block folds the partials; each thread encodes 32
+//             consecutive elements).  Used for tensors larger than the
+//             registers of a resident grid.
+//
+// The block amax is taken on the 15-bit magnitude pattern, which orders like
+// the value for finite bf16.  With K % 32 == 0 a 32-element unit never crosses
+// a row, and the outputs are dense in unit order; the input may be row-strided
+// (a KV append can read the K and V column slices of a fused QKV output in
+// place).
+#include <atomic>
+#include <chrono>
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -84,9 +99,8 @@ __global__ void __launch_bounds__(kThreads) k_amax(QuantArgs args) {
   }
 }
 
-// Folds the amax partials of one tensor into (g, 6g).  Every block does this.
-__device__ __forceinline__ void block_global_scale(const QuantTensor &T, int nparts,
-                                                   float &g, float &six_g) {
+// Folds the amax partials of one tensor into g.  Every block does this.
+__device__ __forceinline__ float block_global_scale(const QuantTensor &T, int nparts) {
   __shared__ uint32_t red[kThreads / 64];
   uint32_t m = 0;
   for (int p = threadIdx.x; p < nparts; p += kThreads) {
@@ -99,9 +113,7 @@ __device__ __forceinline__ void block_global_scale(const QuantTensor &T, int npa
   uint32_t r = red[0];
 #pragma unroll
   for (int w = 1; w < kThreads / 64; ++w) r = r > red[w] ? r : red[w];
-  const float A = bf16_bits_to_f32(r);
-  g = (r == 0) ? 1.0f : A / kGlobalDivisor;                // fl(A / 2688)
-  six_g = kE2M1Max * g;                                      // fl(6·g)
+  return (r == 0) ? 1.0f : bf16_bits_to_f32(r) / kGlobalDivisor;   // fl(A / 2688)
 }
 
 // E2M1 codes of the bf16 pair w scaled by r, written into byte SEL of old
@@ -113,19 +125,58 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t old, uint32_t w, float r) 
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, x0 * r, x1 * r, 1.0f, SEL);
 }
 
-// Encodes one 16-element block held as 8 bf16 pairs; returns the scale byte
-// and writes the 8 code bytes to lo/hi (element 2j in the low nibble of byte j).
-__device__ __forceinline__ uint32_t encode_block16(const uint32_t (&w)[8], float g, float six_g,
-                                                   uint32_t &lo, uint32_t &hi) {
+// Per-tensor constants of the block-scale arithmetic.  Both divisions of a
+// block are done with FMA refinements that return the correctly rounded
+// binary32 result:
+//   s_raw = fl(a / 6g): a and 6g are first scaled by the same power of two
+//     (exact) so 6g lies in [1, 2); then q0 = a·y with y = fl(1/6g), the
+//     residual a − q0·6g (exact by FMA) and q0 + residual·y rounded once give
+//     the correctly rounded quotient (Markstein's theorem; an exhaustive CPU
+//     check over the input domain finds no E4M3 byte that differs);
+//   r = fl(1/d): one Newton step y0 + y0·(1 − d·y0) from the hardware
+//     reciprocal (within 1 ulp) rounds correctly for every binary32
+//     significand (checked exhaustively on the CPU).
+struct BlockScaler {
+  float g, sc, bs, y;
+  __device__ __forceinline__ explicit BlockScaler(float g_) : g(g_) {
+    const float six_g = kE2M1Max * g;                             // fl(6·g)
+    sc = __uint_as_float((254u - ((__float_as_uint(six_g) >> 23) & 0xFFu)) << 23);   // 2^-e(6g)
+    bs = six_g * sc;
+    y = 1.0f / bs;
+  }
+  // E4M3 scale byte of a block whose largest magnitude has bf16 pattern bm.
+  __device__ __forceinline__ uint32_t scale_byte(uint32_t bm) const {
+    const float as = bf16_bits_to_f32(bm) * sc;
+    const float q0 = as * y;
+    const float res = __builtin_fmaf(-q0, bs, as);
+    return e4m3_encode_rne_sat(__builtin_fmaf(res, y, q0));       // fl(a / 6g) → E4M3
+  }
+  // fl(1 / fl(S·g)), 0 for S == 0.
+  __device__ __forceinline__ float recip(uint32_t S) const {
+    const float d = e4m3_decode(S) * g;                           // fl(S·g)
+    const float y0 = __builtin_amdgcn_rcpf(d);
+    const float e = __builtin_fmaf(-d, y0, 1.0f);
+    const float r = __builtin_fmaf(e, y0, y0);
+    return S == 0 ? 0.0f : r;
+  }
+};
+
+// Largest magnitude (bf16 pattern) of 8 bf16 pairs.
+__device__ __forceinline__ uint32_t absmax16(const uint32_t (&w)[8]) {
   uint32_t m = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) m = absmax_bf16x2(m, w[j]);
-  uint32_t mm = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-  const float a = bf16_bits_to_f32(mm);
-  const float s_raw = a / six_g;                             // fl(a / 6g)
-  const uint32_t S = e4m3_encode_rne_sat(s_raw);
-  const float d = e4m3_decode(S) * g;                        // fl(S·g)
-  const float r = (S == 0) ? 0.0f : 1.0f / d;                // fl(1/d)
+  return (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+}
+
+// Encodes one 16-element block held as 8 bf16 pairs whose largest magnitude
+// is bm; returns the scale byte and writes the 8 code bytes to lo/hi (element
+// 2j in the low nibble of byte j).
+__device__ __forceinline__ uint32_t encode_block16(const uint32_t (&w)[8], uint32_t bm,
+                                                   const BlockScaler &bsc, uint32_t &lo,
+                                                   uint32_t &hi) {
+  const uint32_t S = bsc.scale_byte(bm);
+  const float r = bsc.recip(S);
   uint32_t c0 = 0, c1 = 0;
   c0 = cvt_pair<0>(c0, w[0], r);
   c0 = cvt_pair<1>(c0, w[1], r);
@@ -142,8 +193,8 @@ __device__ __forceinline__ uint32_t encode_block16(const uint32_t (&w)[8], float
 
 __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts) {
   const QuantTensor &T = args.t[blockIdx.y];
-  float g, six_g;
-  block_global_scale(T, nparts, g, six_g);
+  const float g = block_global_scale(T, nparts);
+  const BlockScaler bsc(g);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *T.gscale = g;
     if (blockIdx.y == 0 && args.mark.chunk_start != nullptr) {
@@ -158,12 +209,253 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
     uint32_t b0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t b1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
     uint32_t c0, c1, c2, c3;
-    const uint32_t s0 = encode_block16(b0, g, six_g, c0, c1);
-    const uint32_t s1 = encode_block16(b1, g, six_g, c2, c3);
+    const uint32_t s0 = encode_block16(b0, absmax16(b0), bsc, c0, c1);
+    const uint32_t s1 = encode_block16(b1, absmax16(b1), bsc, c2, c3);
     reinterpret_cast<u32x4 *>(T.codes)[u] = u32x4{c0, c1, c2, c3};
     T.scales[u] = (uint16_t)(s0 | (s1 << 8));
   }
 }
+
+// ---------------------------------------------------------------------------
+// Resident single-pass quantiser.
+
+// Slot words: bits 63..16 the call's epoch, bits 15..0 a bf16 magnitude.
+constexpr uint64_t kEpochMask = (uint64_t(1) << 48) - 1;
+constexpr uint64_t kWaitTicks = 100000;       // 1 ms of the 100 MHz real-time counter
+
+// First 16-byte half of 16-element block b of the tensor (unit order).
+__device__ __forceinline__ const u32x4 *block_src(const QuantTensor &T, int64_t b) {
+  return unit_src(T, b >> 1) + 2 * (b & 1);
+}
+
+__device__ __forceinline__ uint64_t load_slot(const uint64_t *slot) {
+  return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Largest value of m over the NT threads of the workgroup (red: NT/64 words).
+template <int NT>
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t *red) {
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = r > red[w] ? r : red[w];
+  return r;
+}
+
+// |x| maximum of a whole tensor read by one workgroup of NT threads (the
+// fallback when the other workgroups' maxima do not arrive in time).
+template <int NT>
+__device__ uint32_t tensor_max_direct(const QuantTensor &T, uint32_t *red) {
+  uint32_t m = 0;
+  for (int64_t b = threadIdx.x; b < 2 * T.units; b += NT) {
+    const u32x4 *p = block_src(T, b);
+    const u32x4 lo = p[0], hi = p[1];
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const uint32_t a = absmax16(w);
+    m = m > a ? m : a;
+  }
+  return block_max_u32<NT>(m, red);
+}
+
+constexpr int kResThreads = 1024;            // one workgroup per CU
+
+// Workgroup k owns, in each of the NJ tensors, the 16-element blocks
+// (k·u + i)·1024 + thread, i < u <= UMAX; a thread loads a block as two
+// 16-byte halves and keeps it in registers.  Each workgroup publishes its
+// maximum per tensor in slot k, then polls all slots of the grid (one load per
+// thread), so every workgroup derives A itself after one round trip.  The wait
+// is bounded: if it expires (the grid was not resident all at once), the
+// workgroup reads the whole tensor itself, which yields the same A, so the
+// result never depends on scheduling.
+template <int NJ, int UMAX>
+__global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, uint64_t epoch,
+                                                                int u) {
+  constexpr int NW = kResThreads / 64;
+  __shared__ uint32_t red[NJ][NW];
+  __shared__ uint32_t shared_A[NJ];
+  const int k = blockIdx.x, nwg = gridDim.x;
+
+  uint32_t w[NJ][UMAX][8], bm[NJ][UMAX];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const QuantTensor &T = args.t[j];
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) {
+      const int64_t b = ((int64_t)k * u + i) * kResThreads + threadIdx.x;
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (i < u && b < 2 * T.units) {
+        const u32x4 *p = block_src(T, b);
+        lo = p[0];
+        hi = p[1];
+      }
+      w[j][i][0] = lo.x; w[j][i][1] = lo.y; w[j][i][2] = lo.z; w[j][i][3] = lo.w;
+      w[j][i][4] = hi.x; w[j][i][5] = hi.y; w[j][i][6] = hi.z; w[j][i][7] = hi.w;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) {
+      bm[j][i] = absmax16(w[j][i]);
+      m = m > bm[j][i] ? m : bm[j][i];
+    }
+    const uint32_t bmax = block_max_u32<kResThreads>(m, red[j]);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(reinterpret_cast<uint64_t *>(args.t[j].partials) + k, (epoch << 16) | bmax,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // poll: thread p < nwg watches slot p of every tensor
+  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kWaitTicks;
+  uint32_t a[NJ], pending = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    a[j] = 0;
+    if ((int)threadIdx.x < nwg) pending |= 1u << j;
+  }
+  bool done = false;
+  while (true) {
+    uint64_t sw[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      sw[j] = (pending >> j) & 1u
+                  ? load_slot(reinterpret_cast<const uint64_t *>(args.t[j].partials) + threadIdx.x)
+                  : 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (((pending >> j) & 1u) && (sw[j] >> 16) == epoch) {
+        a[j] = (uint32_t)(sw[j] & 0xFFFFu);
+        pending &= ~(1u << j);
+      }
+    if (__syncthreads_and(pending == 0)) {
+      done = true;
+      break;
+    }
+    if (__syncthreads_or(__builtin_amdgcn_s_memrealtime() > deadline)) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __syncthreads();                          // red[] is read below
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const uint32_t A = done ? block_max_u32<kResThreads>(a[j], red[j])
+                            : tensor_max_direct<kResThreads>(args.t[j], red[j]);
+    if (threadIdx.x == 0) shared_A[j] = A;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const QuantTensor &T = args.t[j];
+    const uint32_t Abits = shared_A[j];
+    const float g = (Abits == 0) ? 1.0f : bf16_bits_to_f32(Abits) / kGlobalDivisor;
+    const BlockScaler bsc(g);
+    if (k == 0 && threadIdx.x == 0) {
+      *T.gscale = g;
+      if (j == 0 && args.mark.chunk_start != nullptr) {
+        args.mark.chunk_start[args.mark.index] = args.mark.value;
+        if (args.mark.index == 1) args.mark.chunk_start[0] = 0;
+      }
+    }
+    u32x2 *codes = reinterpret_cast<u32x2 *>(T.codes);
+    uint8_t *scales = reinterpret_cast<uint8_t *>(T.scales);
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) {
+      const int64_t b = ((int64_t)k * u + i) * kResThreads + threadIdx.x;
+      uint32_t lo, hi;
+      const uint32_t S = encode_block16(w[j][i], bm[j][i], bsc, lo, hi);
+      if (i < u && b < 2 * T.units) {
+        codes[b] = u32x2{lo, hi};
+        scales[b] = (uint8_t)S;
+      }
+    }
+  }
+}
+
+// Resident-launch limits of a device: CU count and whether each kernel
+// instance fits one workgroup per CU.
+struct ResidentLimits {
+  int cus = 0;
+  bool fits[2][4] = {};                   // [NJ - 1][log2 UMAX]
+};
+
+template <int NJ, int UMAX>
+static const void *resident_fn() {
+  return reinterpret_cast<const void *>(&k_quant_resident<NJ, UMAX>);
+}
+
+static const ResidentLimits &resident_limits() {
+  static std::mutex mu;
+  static ResidentLimits table[64];
+  static bool filled[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!filled[dev]) {
+    ResidentLimits &r = table[dev];
+    if (hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) r.cus = 0;
+    const void *fns[2][4] = {
+        {resident_fn<1, 1>(), resident_fn<1, 2>(), resident_fn<1, 4>(), resident_fn<1, 8>()},
+        {resident_fn<2, 1>(), resident_fn<2, 2>(), resident_fn<2, 4>(), nullptr}};
+    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i) {
+        int n = 0;
+        r.fits[j][i] = fns[j][i] != nullptr &&
+                       hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fns[j][i], kResThreads, 0) ==
+                           hipSuccess &&
+                       n >= 1;
+      }
+    filled[dev] = true;
+  }
+  return table[dev];
+}
+
+// Epochs identify a call's slot words; they only need to differ between calls
+// that share a workspace and from whatever the workspace held before.
+static uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{
+      (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
+  uint64_t e = counter.fetch_add(1) & kEpochMask;
+  return e == 0 ? 1 : e;
+}
+
+// Launches the resident quantiser (at most one workgroup per CU) when the
+// tensors fit in its registers; returns false (nothing launched) otherwise.
+static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStream_t stream,
+                            hipError_t *err) {
+  const ResidentLimits &lim = resident_limits();
+  if (lim.cus < 1) return false;
+  const int64_t nb = 2 * max_units;                         // 16-element blocks per tensor
+  int64_t nwg = (nb + kResThreads - 1) / kResThreads;
+  if (nwg > lim.cus) nwg = lim.cus;
+  if (nwg > kResidentSlots) nwg = kResidentSlots;
+  const int64_t u = (nb + nwg * kResThreads - 1) / (nwg * kResThreads);
+  int li = 0;
+  while (li < 4 && (1 << li) < u) ++li;
+  if (li == 4 || !lim.fits[njobs - 1][li]) return false;
+  const uint64_t epoch = next_epoch();
+  const dim3 grid((unsigned)nwg), block(kResThreads);
+  const int ui = (int)u;
+  if (njobs == 1) {
+    switch (li) {
+      case 0: hipLaunchKernelGGL((k_quant_resident<1, 1>), grid, block, 0, stream, a, epoch, ui); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<1, 2>), grid, block, 0, stream, a, epoch, ui); break;
+      case 2: hipLaunchKernelGGL((k_quant_resident<1, 4>), grid, block, 0, stream, a, epoch, ui); break;
+      default: hipLaunchKernelGGL((k_quant_resident<1, 8>), grid, block, 0, stream, a, epoch, ui); break;
+    }
+  } else {
+    switch (li) {
+      case 0: hipLaunchKernelGGL((k_quant_resident<2, 1>), grid, block, 0, stream, a, epoch, ui); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<2, 2>), grid, block, 0, stream, a, epoch, ui); break;
+      default: hipLaunchKernelGGL((k_quant_resident<2, 4>), grid, block, 0, stream, a, epoch, ui); break;
+    }
+  }
+  *err = hipGetLastError();
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 
 static int amax_blocks(int64_t units) {
   int64_t b = (units + kThreads * 2 - 1) / (kThreads * 2);        // >= 2 units per thread
@@ -195,11 +487,13 @@ hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
     a.t[i].ld = jobs[i].ld;
     if (a.t[i].units > max_units) max_units = a.t[i].units;
   }
+  hipError_t e = hipSuccess;
+  if (launch_resident(a, njobs, max_units, stream, &e)) return e;
   // Both tensors of a pair use the same grid; a tensor with fewer units simply
   // leaves some threads idle.
   const int nparts = amax_blocks(max_units);
   hipLaunchKernelGGL(k_amax, dim3(nparts, njobs), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_encode, dim3(encode_blocks(max_units), njobs), dim3(kThreads), 0, stream, a,
                      nparts);
