@@ -85,9 +85,9 @@ struct Tile {
   static constexpr int BM = 64 * WM, BN = 64 * WN;
   static constexpr int A_CODE = 0;
   static constexpr int W_CODE = A_CODE + kChunks * (BM + kPadRows) * 16;
-  static constexpr int A_SCALE = W_CODE + kChunks * (BN + kPadRows) * 16;
-  static constexpr int W_SCALE = A_SCALE + BM * 8;
-  static constexpr int STAGE = W_SCALE + BN * 8;
+  static constexpr int A_SCALE = W_CODE + kChunks * (BN + kPadRows) * 16;   // [2][BM][4 pairs]
+  static constexpr int W_SCALE = A_SCALE + BM * 32;
+  static constexpr int STAGE = W_SCALE + BN * 32;
   static constexpr int LDS = 2 * STAGE;
 };
 
@@ -140,6 +140,11 @@ __device__ __forceinline__ void fill_load(Fill<ROWS> &f, const Operand &op, int6
   }
 }
 
+// Codes go to LDS as they are; the 8 scale bytes of a row are expanded to
+// fp16 scale pairs (scale_pair_f16) and stored as two 16-byte groups, blocks
+// {0, 1, 4, 5} in the first ROWS·16 bytes and {2, 3, 6, 7} in the next: group
+// h holds the blocks 2h, 2h+1, 4+2h, 5+2h that a lane with that h decodes, and
+// a wave's accesses to one group are contiguous.
 template <int ROWS>
 __device__ __forceinline__ void fill_store(const Fill<ROWS> &f, uint8_t *code_lds, uint8_t *scale_lds) {
   const int t = threadIdx.x;
@@ -150,15 +155,20 @@ __device__ __forceinline__ void fill_store(const Fill<ROWS> &f, uint8_t *code_ld
     *reinterpret_cast<u32x4 *>(code_lds + (c * (ROWS + kPadRows) + row) * 16) = f.code[it];
   }
   const int srow = t < ROWS ? t : ROWS - 1;
-  *reinterpret_cast<u32x2 *>(scale_lds + srow * 8) = f.scale;
+  const uint32_t lo = f.scale.x, hi = f.scale.y;     // blocks 0..3, 4..7
+  const u32x4 g0 = {scale_pair_f16(lo), scale_pair_f16(lo >> 8), scale_pair_f16(hi), scale_pair_f16(hi >> 8)};
+  const u32x4 g1 = {scale_pair_f16(lo >> 16), scale_pair_f16(lo >> 24), scale_pair_f16(hi >> 16),
+                    scale_pair_f16(hi >> 24)};
+  *reinterpret_cast<u32x4 *>(scale_lds + srow * 16) = g0;
+  *reinterpret_cast<u32x4 *>(scale_lds + (ROWS + srow) * 16) = g1;
 }
 
-// A wave's view of one stage: codes of both sub-steps and the 8 scale bytes,
-// per row block q (A blocks first, then W blocks).
+// A wave's view of one stage: codes of both sub-steps and the lane's four
+// fp16 scale pairs, per row block q (A blocks first, then W blocks).
 template <int NQ>
 struct Frag {
   u32x4 c[2][NQ];
-  u32x2 sc[NQ];
+  u32x4 sc[NQ];
 };
 
 template <int WM, int WN>
@@ -168,7 +178,7 @@ __device__ __forceinline__ void frag_read(Frag<WM + WN> &fr, const uint8_t *buf,
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
     const int row = wm * 32 * WM + 32 * i + r;
-    fr.sc[i] = *reinterpret_cast<const u32x2 *>(buf + T::A_SCALE + row * 8);
+    fr.sc[i] = *reinterpret_cast<const u32x4 *>(buf + T::A_SCALE + (h * T::BM + row) * 16);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       fr.c[s][i] = *reinterpret_cast<const u32x4 *>(buf + T::A_CODE + ((2 * s + h) * (T::BM + kPadRows) + row) * 16);
@@ -176,7 +186,7 @@ __device__ __forceinline__ void frag_read(Frag<WM + WN> &fr, const uint8_t *buf,
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     const int row = wn * 32 * WN + 32 * j + r;
-    fr.sc[WM + j] = *reinterpret_cast<const u32x2 *>(buf + T::W_SCALE + row * 8);
+    fr.sc[WM + j] = *reinterpret_cast<const u32x4 *>(buf + T::W_SCALE + (h * T::BN + row) * 16);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       fr.c[s][WM + j] = *reinterpret_cast<const u32x4 *>(buf + T::W_CODE + ((2 * s + h) * (T::BN + kPadRows) + row) * 16);
@@ -184,15 +194,13 @@ __device__ __forceinline__ void frag_read(Frag<WM + WN> &fr, const uint8_t *buf,
 }
 
 // Decode step T (0..7) of a stage into fragments f: dword T%4 of sub-step T/4,
-// block 4·(T/4) + 2h + (T%4)/2 of the stage → byte (T%4)/2 of the lane's pair.
+// block 4·(T/4) + 2h + (T%4)/2 of the stage → scale pair 2·(T/4) + (T%4)/2 of
+// the lane's group.
 template <int T, int NQ>
-__device__ __forceinline__ void decode_step(const Frag<NQ> &fr, int h, f16x8 (&f)[NQ]) {
+__device__ __forceinline__ void decode_step(const Frag<NQ> &fr, int, f16x8 (&f)[NQ]) {
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const uint32_t pair = (T < 4 ? fr.sc[q].x : fr.sc[q].y) >> (16 * h);
-    const uint32_t sp = scale_pair_f16(pair >> (8 * ((T & 3) >> 1)));
-    f[q] = decode8(fr.c[T >> 2][q][T & 3], sp);
-  }
+  for (int q = 0; q < NQ; ++q)
+    f[q] = decode8(fr.c[T >> 2][q][T & 3], fr.sc[q][2 * (T >> 2) + ((T & 3) >> 1)]);
 }
 
 template <int WM, int WN>
