@@ -23,13 +23,18 @@ Parity status per function:
   formats.bf16_*         pinned (torch cast on f32 inputs, hand double-rounding cases)
   nvfp4.quantize         pinned (hand-worked golden block, lossless round trip,
                          amax→±6, sign and power-of-two invariances)
+  nvfp4.quantize(adaptive46=True), nvfp4.block_sq_error
+                         pinned (hand-worked golden blocks with their errors,
+                         lossless on the amax→4 grid, never worse than amax→6
+                         in binary64, exact-rational choice, invariances)
   nvfp4.dequantize       pinned (dequant equation on round-trip inputs)
   nvfp4.gemm_ref         pinned (Fraction brute force, unit-scale special case,
                          global-scale linearity, block-sum form)
   nvfp4.gelu_tanh        pinned (gelu(0)=0, gelu(y)-gelu(-y)=y, large-|y| limits)
   nvfp4.KVCacheRef       pinned (byte closed form from the pages, append ≡ quantize)
   The choices of global-scale formula, scale rounding mode, reciprocal-multiply
-  order, nibble order and per-append KV scale are fixed by definition only
+  order, nibble order, per-append KV scale and the binary32 error order of the
+  adaptive selection are fixed by definition only
   ("parity unpinned" for those choices; see the readings in the design notes).
 """
 
@@ -47,6 +52,7 @@ from .formats import (
 from .nvfp4 import (
     GLOBAL_DIVISOR,
     quantize,
+    block_sq_error,
     dequantize,
     gemm_ref,
     gelu_tanh,
@@ -66,6 +72,7 @@ __all__ = [
     "unpack_nibbles",
     "GLOBAL_DIVISOR",
     "quantize",
+    "block_sq_error",
     "dequantize",
     "gemm_ref",
     "gelu_tanh",

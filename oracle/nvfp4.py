@@ -28,6 +28,14 @@ Where the pages leave a step open, the readings taken are:
   R11 an all-zero tensor gets g = 1;
   R12 inputs are finite and A is 0 or >= 2^-100;
   R15 the KV cache keeps one g per append call per tensor.  [parity unpinned]
+  R23 adaptive block scales (二、方法 / 推理底座 and the distillation paragraph of
+      二、方法 name an "adaptive scale" search over the amax targets {4, 6}):
+      each block is encoded twice, with its amax mapped to 6 (as above) and
+      to 4 (divisor fl(4·g) in place of fl(6·g)); the encoding whose block
+      squared error is smaller is kept, ties to 6;
+  R24 that error is computed in binary32, element by element in index order:
+      deq = fl(fl(E2M1·S)·g) with the code's sign, e = fl(x − deq),
+      err = fl(err + fl(e·e)) from err = 0.            [parity unpinned]
 """
 
 from __future__ import annotations
@@ -53,13 +61,47 @@ E4M3_MAX = 448.0                # largest finite E4M3 value
 GLOBAL_DIVISOR = np.float32(E2M1_MAX * E4M3_MAX)   # 2688, exact in binary32
 
 
-def quantize(x_bits: np.ndarray, amax=None):
+def _encode_blocks(blocks, g, target):
+    """Scale bytes and E2M1 magnitude codes of blocks [M, nb, 16] (|x|, binary32)
+    with each block's amax mapped to ``target`` (6 or 4): the steps R4-R7, R10."""
+    div = np.float32(np.float32(target) * g)                 # fl(target·g)
+    a_blk = blocks.max(axis=2)                               # exact
+    s_raw = (a_blk / div).astype(np.float32)                 # fl(a / (target·g))
+    S = e4m3_encode_rne_satfinite(s_raw.astype(np.float64))  # RNE, satfinite
+    S_val = e4m3_decode(S).astype(np.float32)                # exact in f32
+    d = (S_val * g).astype(np.float32)                       # fl(S·g)
+    with np.errstate(divide="ignore"):
+        r = np.where(S == 0, np.float32(0.0), (np.float32(1.0) / d)).astype(np.float32)
+    q = (blocks * r[:, :, None]).astype(np.float32)          # fl(|x|·r)
+    m = e2m1_rne_sat(q.astype(np.float64))
+    return S.astype(np.uint8), m.astype(np.uint8)
+
+
+def block_sq_error(x, S, m, neg, g):
+    """R24: per-block squared error of an encoding, in binary32, in index order.
+
+    ``x`` [M, nb, 16] float32 values, ``S`` [M, nb] scale bytes, ``m`` [M, nb, 16]
+    magnitude codes, ``neg`` [M, nb, 16] sign flags, ``g`` the tensor scale."""
+    S_val = e4m3_decode(S).astype(np.float32)
+    mag = E2M1_VALUES[m].astype(np.float32)
+    deq = ((mag * S_val[:, :, None]).astype(np.float32) * np.float32(g)).astype(np.float32)
+    deq = np.where(neg, -deq, deq).astype(np.float32)
+    e = (x - deq).astype(np.float32)
+    err = np.zeros(S.shape, dtype=np.float32)
+    for i in range(BLOCK):
+        err = (err + (e[:, :, i] * e[:, :, i]).astype(np.float32)).astype(np.float32)
+    return err
+
+
+def quantize(x_bits: np.ndarray, amax=None, adaptive46=False):
     """NVFP4-quantise a bf16 matrix ``x`` [M, K] (given as uint16 bit patterns).
 
     Returns ``(codes u8 [M, K/2], scales u8 [M, K/16], g float32)``.
 
     Rows are independent once the tensor amax A is known, so a caller may pass
     a subset of a tensor's rows together with ``amax`` = that tensor's A.
+    ``adaptive46`` selects, per block, the better of the amax→6 and amax→4
+    encodings (R23, R24); the output format is unchanged.
 
     The steps, in binary32 (each line one IEEE operation, nearest-even):
       A = max |x|                              (exact)
@@ -95,21 +137,20 @@ def quantize(x_bits: np.ndarray, amax=None):
         raise ValueError("tensor amax below 2^-100 is outside the domain (R12)")
 
     g = np.float32(A / GLOBAL_DIVISOR)                       # fl(A / 2688)
-    six_g = np.float32(np.float32(E2M1_MAX) * g)             # fl(6·g)
 
     blocks = ax.reshape(M, K // BLOCK, BLOCK)
-    a_blk = blocks.max(axis=2)                               # exact
-    s_raw = (a_blk / six_g).astype(np.float32)               # fl(a / 6g)
-    S = e4m3_encode_rne_satfinite(s_raw.astype(np.float64))  # RNE, satfinite
-    S_val = e4m3_decode(S).astype(np.float32)                # exact in f32
-    d = (S_val * g).astype(np.float32)                       # fl(S·g)
-    with np.errstate(divide="ignore"):
-        r = np.where(S == 0, np.float32(0.0), (np.float32(1.0) / d)).astype(np.float32)
-
-    q = (blocks * r[:, :, None]).astype(np.float32)          # fl(|x|·r)
-    m = e2m1_rne_sat(q.astype(np.float64)).reshape(M, K)
-    code = (sign | m).astype(np.uint8)
-    return pack_nibbles(code), S.astype(np.uint8), g
+    S, m = _encode_blocks(blocks, g, E2M1_MAX)
+    if adaptive46:
+        S4, m4 = _encode_blocks(blocks, g, 4.0)
+        xb = x.reshape(M, K // BLOCK, BLOCK)
+        neg = (sign.reshape(M, K // BLOCK, BLOCK) != 0)
+        e6 = block_sq_error(xb, S, m, neg, g)
+        e4 = block_sq_error(xb, S4, m4, neg, g)
+        use4 = e4 < e6                                       # ties keep 6
+        S = np.where(use4, S4, S).astype(np.uint8)
+        m = np.where(use4[:, :, None], m4, m).astype(np.uint8)
+    code = (sign | m.reshape(M, K)).astype(np.uint8)
+    return pack_nibbles(code), S, g
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, g) -> np.ndarray:
@@ -209,15 +250,15 @@ class KVCacheRef:
         self.chunk_start = [0]
         self.n_tokens = 0
 
-    def append(self, k_bits: np.ndarray, v_bits: np.ndarray):
+    def append(self, k_bits: np.ndarray, v_bits: np.ndarray, adaptive46=False):
         T = k_bits.shape[0]
         if k_bits.shape != (T, self.H, self.D) or v_bits.shape != k_bits.shape:
             raise ValueError("K and V must be [T, H, D]")
         if self.n_tokens + T > self.cap:
             raise ValueError("capacity exceeded")
         n = self.n_tokens
-        kc, ks, kg = quantize(k_bits.reshape(T * self.H, self.D))
-        vc, vs, vg = quantize(v_bits.reshape(T * self.H, self.D))
+        kc, ks, kg = quantize(k_bits.reshape(T * self.H, self.D), adaptive46=adaptive46)
+        vc, vs, vg = quantize(v_bits.reshape(T * self.H, self.D), adaptive46=adaptive46)
         self.k_codes[n:n + T] = kc.reshape(T, self.H, -1)
         self.k_scales[n:n + T] = ks.reshape(T, self.H, -1)
         self.v_codes[n:n + T] = vc.reshape(T, self.H, -1)
