@@ -19,6 +19,7 @@ import torch
 from ._lib import (  # noqa: F401
     LIB_PATH,
     NVFP4_EPI_GELU_TANH,
+    NVFP4_Q_ADAPTIVE_4_6,
     NVFP4_TILES,
     KVCacheDesc,
     NVFP4Error,
@@ -64,20 +65,23 @@ def linear_workspace_bytes(M: int, K: int) -> int:
     return n.value
 
 
-def quantize_into(x, codes, scales, gscale, ws):
-    """nvfp4_quantize into caller-provided tensors (no allocation)."""
+def quantize_into(x, codes, scales, gscale, ws, adaptive46=False):
+    """nvfp4_quantize (nvfp4_quantize_ex with NVFP4_Q_ADAPTIVE_4_6 when
+    ``adaptive46``) into caller-provided tensors (no allocation)."""
     M, K = x.shape
     _need(x, torch.bfloat16, "x")
     _need(codes, torch.uint8, "codes", (M, K // 2))
     _need(scales, torch.uint8, "scales", (M, K // 16))
     _need(gscale, torch.float32, "gscale", (1,))
     _need(ws, torch.uint8, "ws")
-    check(lib().nvfp4_quantize(_ptr(x), M, K, _ptr(codes), _ptr(scales), _ptr(gscale),
-                               _ptr(ws), ws.numel(), _stream(x.device)))
+    qflags = NVFP4_Q_ADAPTIVE_4_6 if adaptive46 else 0
+    check(lib().nvfp4_quantize_ex(_ptr(x), M, K, qflags, _ptr(codes), _ptr(scales), _ptr(gscale),
+                                  _ptr(ws), ws.numel(), _stream(x.device)))
 
 
-def quantize(x: torch.Tensor):
-    """bf16 [M, K] → (codes u8 [M, K/2], scales u8 [M, K/16], gscale f32 [1])."""
+def quantize(x: torch.Tensor, adaptive46=False):
+    """bf16 [M, K] → (codes u8 [M, K/2], scales u8 [M, K/16], gscale f32 [1]);
+    ``adaptive46`` selects the adaptive {4, 6} block scales."""
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
@@ -86,7 +90,7 @@ def quantize(x: torch.Tensor):
     scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     gscale = torch.empty((1,), dtype=torch.float32, device=dev)
     ws = torch.empty((quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
-    quantize_into(x, codes, scales, gscale, ws)
+    quantize_into(x, codes, scales, gscale, ws, adaptive46)
     return codes, scales, gscale
 
 
@@ -182,10 +186,11 @@ class KVCache:
         check(lib().nvfp4_kv_append_workspace(T, self.desc.heads, self.desc.head_dim, C.byref(n)))
         return n.value
 
-    def append(self, K, V, ws=None):
+    def append(self, K, V, ws=None, adaptive46=False):
         """Append K, V: bf16 [T, heads, head_dim] tensors, or [T, ld] row views
         (e.g. column slices of a fused QKV output) whose rows hold
-        heads·head_dim contiguous values."""
+        heads·head_dim contiguous values.  ``adaptive46`` selects the adaptive
+        {4, 6} block scales for this append."""
         T = K.shape[0]
         HD = self.desc.heads * self.desc.head_dim
         for t, name in ((K, "K"), (V, "V")):
@@ -205,8 +210,9 @@ class KVCache:
             if self._ws is None or self._ws.numel() < self.workspace_bytes(T):
                 self._ws = torch.empty((self.workspace_bytes(T),), dtype=torch.uint8, device=self.device)
             ws = self._ws
-        check(lib().nvfp4_kv_append(C.byref(self.desc), _ptr(K), _ptr(V), T, ld, _ptr(ws), ws.numel(),
-                                    _stream(self.device)))
+        qflags = NVFP4_Q_ADAPTIVE_4_6 if adaptive46 else 0
+        check(lib().nvfp4_kv_append_ex(C.byref(self.desc), _ptr(K), _ptr(V), T, ld, qflags, _ptr(ws),
+                                       ws.numel(), _stream(self.device)))
 
     def reset(self):
         """Forget every token (host counters only; enqueues nothing)."""

@@ -21,6 +21,7 @@ NVFP4_EWORKSPACE = 2
 NVFP4_ECAPACITY = 3
 NVFP4_EHIP = 4
 NVFP4_EPI_GELU_TANH = 0x1
+NVFP4_Q_ADAPTIVE_4_6 = 0x10
 NVFP4_TILES = {(256, 256): 0x100, (256, 192): 0x200, (192, 256): 0x300, (256, 128): 0x400,
                (128, 256): 0x500, (128, 128): 0x600}
 
@@ -43,6 +44,7 @@ class KVCacheDesc(C.Structure):
 _SIGS = {
     "nvfp4_quantize_workspace": ([_i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_quantize": ([_p, _i64, _i64, _p, _p, _p, _p, _sz, _p], C.c_int),
+    "nvfp4_quantize_ex": ([_p, _i64, _i64, C.c_uint32, _p, _p, _p, _p, _sz, _p], C.c_int),
     "nvfp4_gemm": ([_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i64, C.c_uint32, _p], C.c_int),
     "nvfp4_gemm_tile": ([_i64, _i64, _i64, C.POINTER(C.c_int), C.POINTER(C.c_int)], C.c_int),
     "nvfp4_linear_workspace": ([_i64, _i64, C.POINTER(_sz)], C.c_int),
@@ -50,6 +52,8 @@ _SIGS = {
     "nvfp4_kv_init": ([C.POINTER(KVCacheDesc)], C.c_int),
     "nvfp4_kv_append_workspace": ([_i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_kv_append": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _i64, _p, _sz, _p], C.c_int),
+    "nvfp4_kv_append_ex": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _i64, C.c_uint32, _p, _sz, _p],
+                           C.c_int),
     "nvfp4_kv_dequant": ([C.POINTER(KVCacheDesc), _i64, _i64, _p, _p, _p], C.c_int),
     "nvfp4_strerror": ([C.c_int], C.c_char_p),
     "nvfp4_last_error": ([], C.c_char_p),

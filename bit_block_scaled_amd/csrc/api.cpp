@@ -99,10 +99,11 @@ int nvfp4_quantize_workspace(int64_t M, int64_t K, size_t *bytes) {
   return NVFP4_OK;
 }
 
-int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
-                   float *gscale, void *ws, size_t ws_bytes, void *stream) {
+int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags, uint8_t *codes,
+                      uint8_t *scales, float *gscale, void *ws, size_t ws_bytes, void *stream) {
   int s;
   if ((s = check_mk(M, K, "quantize"))) return s;
+  if (qflags & ~NVFP4_Q_ADAPTIVE_4_6) return fail(NVFP4_EINVAL, "quantize: unknown flags");
   if ((s = check_ptr(x, "x"))) return s;
   if ((s = check_ptr(codes, "codes"))) return s;
   if ((s = check_ptr(scales, "scales"))) return s;
@@ -110,7 +111,14 @@ int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint
   if (ws == nullptr || ws_bytes < kQuantWs) return fail(NVFP4_EWORKSPACE, "quantize: workspace too small");
   if ((s = check_ptr(ws, "ws"))) return s;
   nvfp4::QuantJob j{x, codes, scales, gscale, static_cast<uint32_t *>(ws), M, K, K};
-  return hip_status(nvfp4::launch_quantize(&j, 1, static_cast<hipStream_t>(stream)), "quantize");
+  return hip_status(nvfp4::launch_quantize(&j, 1, static_cast<hipStream_t>(stream), nullptr,
+                                           (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0),
+                    "quantize");
+}
+
+int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
+                   float *gscale, void *ws, size_t ws_bytes, void *stream) {
+  return nvfp4_quantize_ex(x, M, K, 0u, codes, scales, gscale, ws, ws_bytes, stream);
 }
 
 int nvfp4_gemm(const uint8_t *Aq, const uint8_t *As, const float *Ag, const uint8_t *Wq,
@@ -191,10 +199,11 @@ static int check_cache(const nvfp4_kv_cache *c, const char *who) {
   return NVFP4_OK;
 }
 
-int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T, int64_t ld,
-                    void *ws, size_t ws_bytes, void *stream) {
+int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T,
+                       int64_t ld, uint32_t qflags, void *ws, size_t ws_bytes, void *stream) {
   int s;
   if ((s = check_cache(c, "kv_append"))) return s;
+  if (qflags & ~NVFP4_Q_ADAPTIVE_4_6) return fail(NVFP4_EINVAL, "kv_append: unknown flags");
   if (T < 1) return fail(NVFP4_EINVAL, "kv_append: T must be >= 1");
   if (ld < c->heads * c->head_dim || ld % 8) return fail(NVFP4_EINVAL, "kv_append: ld must be >= heads*head_dim and a multiple of 8");
   if (T > kMaxElements / ld) return fail(NVFP4_EINVAL, "kv_append: T*ld too large");
@@ -212,11 +221,18 @@ int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int
       {V, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
        parts + kQuantWs / sizeof(uint32_t), T, e, ld}};
   nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
-  s = hip_status(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark), "kv_append");
+  s = hip_status(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark,
+                                        (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0),
+                 "kv_append");
   if (s) return s;
   c->n_tokens += T;
   c->n_chunks += 1;
   return NVFP4_OK;
+}
+
+int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T, int64_t ld,
+                    void *ws, size_t ws_bytes, void *stream) {
+  return nvfp4_kv_append_ex(c, K, V, T, ld, 0u, ws, ws_bytes, stream);
 }
 
 int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1, uint16_t *K_out,

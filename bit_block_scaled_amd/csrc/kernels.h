@@ -37,8 +37,9 @@ struct ChunkMark {
 
 // Quantises one or two tensors (njobs in {1, 2}) on `stream`: one launch when
 // the grid fits on the device at once, else two launches.
+// adaptive46 selects the adaptive {4, 6} block scales.
 hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
-                           const ChunkMark *mark = nullptr);
+                           const ChunkMark *mark = nullptr, bool adaptive46 = false);
 
 struct GemmArgs {
   const uint8_t *Aq;

@@ -136,12 +136,14 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t old, uint32_t w, float r) 
 //   r = fl(1/d): one Newton step y0 + y0·(1 − d·y0) from the hardware
 //     reciprocal (within 1 ulp) rounds correctly for every binary32
 //     significand (checked exhaustively on the CPU).
+// The block amax maps to `target` (6, or 4 for the second candidate of the
+// adaptive selection), i.e. the divisor is fl(target·g).
 struct BlockScaler {
   float g, sc, bs, y;
-  __device__ __forceinline__ explicit BlockScaler(float g_) : g(g_) {
-    const float six_g = kE2M1Max * g;                             // fl(6·g)
-    sc = __uint_as_float((254u - ((__float_as_uint(six_g) >> 23) & 0xFFu)) << 23);   // 2^-e(6g)
-    bs = six_g * sc;
+  __device__ __forceinline__ BlockScaler(float g_, float target) : g(g_) {
+    const float div = target * g;                                 // fl(target·g)
+    sc = __uint_as_float((254u - ((__float_as_uint(div) >> 23) & 0xFFu)) << 23);   // 2^-e(div)
+    bs = div * sc;
     y = 1.0f / bs;
   }
   // E4M3 scale byte of a block whose largest magnitude has bf16 pattern bm.
@@ -149,7 +151,7 @@ struct BlockScaler {
     const float as = bf16_bits_to_f32(bm) * sc;
     const float q0 = as * y;
     const float res = __builtin_fmaf(-q0, bs, as);
-    return e4m3_encode_rne_sat(__builtin_fmaf(res, y, q0));       // fl(a / 6g) → E4M3
+    return e4m3_encode_rne_sat(__builtin_fmaf(res, y, q0));       // fl(a / div) → E4M3
   }
   // fl(1 / fl(S·g)), 0 for S == 0.
   __device__ __forceinline__ float recip(uint32_t S) const {
@@ -169,14 +171,10 @@ __device__ __forceinline__ uint32_t absmax16(const uint32_t (&w)[8]) {
   return (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
 }
 
-// Encodes one 16-element block held as 8 bf16 pairs whose largest magnitude
-// is bm; returns the scale byte and writes the 8 code bytes to lo/hi (element
-// 2j in the low nibble of byte j).
-__device__ __forceinline__ uint32_t encode_block16(const uint32_t (&w)[8], uint32_t bm,
-                                                   const BlockScaler &bsc, uint32_t &lo,
-                                                   uint32_t &hi) {
-  const uint32_t S = bsc.scale_byte(bm);
-  const float r = bsc.recip(S);
+// E2M1 codes of one 16-element block (8 bf16 pairs) scaled by r: element 2j
+// in the low nibble of byte j, elements 0..7 in lo, 8..15 in hi.
+__device__ __forceinline__ void encode_codes(const uint32_t (&w)[8], float r, uint32_t &lo,
+                                             uint32_t &hi) {
   uint32_t c0 = 0, c1 = 0;
   c0 = cvt_pair<0>(c0, w[0], r);
   c0 = cvt_pair<1>(c0, w[1], r);
@@ -188,13 +186,82 @@ __device__ __forceinline__ uint32_t encode_block16(const uint32_t (&w)[8], uint3
   c1 = cvt_pair<3>(c1, w[7], r);
   lo = c0;
   hi = c1;
+}
+
+// Encodes one 16-element block held as 8 bf16 pairs whose largest magnitude
+// is bm; returns the scale byte and writes the 8 code bytes to lo/hi.
+__device__ __forceinline__ uint32_t encode_block16(const uint32_t (&w)[8], uint32_t bm,
+                                                   const BlockScaler &bsc, uint32_t &lo,
+                                                   uint32_t &hi) {
+  const uint32_t S = bsc.scale_byte(bm);
+  encode_codes(w, bsc.recip(S), lo, hi);
   return S;
 }
 
+// Squared error of elements 2J, 2J+1 of an encoding, added to err in index
+// order: deq = fl(fl(E2M1·S)·g) with the code's sign, e = fl(x − deq),
+// err = fl(err + fl(e·e)).  Every operation rounds on its own.
+template <int J>
+__device__ __forceinline__ float err_pair(float err, uint32_t w, uint32_t codes, float sv, float g) {
+#pragma clang fp contract(off)
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, J & 3);   // signed E2M1
+  const float x0 = bf16_bits_to_f32(w & 0xFFFFu), x1 = bf16_bits_to_f32(w >> 16);
+  const float e0 = x0 - (v.x * sv) * g;
+  err = err + e0 * e0;
+  const float e1 = x1 - (v.y * sv) * g;
+  err = err + e1 * e1;
+  return err;
+}
+
+__device__ __forceinline__ float block_err(const uint32_t (&w)[8], uint32_t lo, uint32_t hi,
+                                           uint32_t S, float g) {
+  const float sv = e4m3_decode(S);
+  float err = 0.0f;
+  err = err_pair<0>(err, w[0], lo, sv, g);
+  err = err_pair<1>(err, w[1], lo, sv, g);
+  err = err_pair<2>(err, w[2], lo, sv, g);
+  err = err_pair<3>(err, w[3], lo, sv, g);
+  err = err_pair<4>(err, w[4], hi, sv, g);
+  err = err_pair<5>(err, w[5], hi, sv, g);
+  err = err_pair<6>(err, w[6], hi, sv, g);
+  err = err_pair<7>(err, w[7], hi, sv, g);
+  return err;
+}
+
+// Adaptive {4, 6} selection: the block is encoded with its amax mapped to 6
+// and to 4; the encoding with the smaller binary32 squared error is kept,
+// ties to 6 (identical scale bytes give identical codes, so no error is
+// computed for them).
+__device__ __forceinline__ uint32_t encode_block16_46(const uint32_t (&w)[8], uint32_t bm,
+                                                      const BlockScaler &b6, const BlockScaler &b4,
+                                                      uint32_t &lo, uint32_t &hi) {
+  const uint32_t S6 = b6.scale_byte(bm), S4 = b4.scale_byte(bm);
+  encode_codes(w, b6.recip(S6), lo, hi);
+  if (S4 == S6) return S6;
+  uint32_t lo4, hi4;
+  encode_codes(w, b4.recip(S4), lo4, hi4);
+  const float e6 = block_err(w, lo, hi, S6, b6.g), e4 = block_err(w, lo4, hi4, S4, b4.g);
+  if (e4 < e6) {
+    lo = lo4;
+    hi = hi4;
+    return S4;
+  }
+  return S6;
+}
+
+// One block in the selected mode.
+template <bool ADAPT>
+__device__ __forceinline__ uint32_t encode_any(const uint32_t (&w)[8], uint32_t bm,
+                                               const BlockScaler &b6, const BlockScaler &b4,
+                                               uint32_t &lo, uint32_t &hi) {
+  return ADAPT ? encode_block16_46(w, bm, b6, b4, lo, hi) : encode_block16(w, bm, b6, lo, hi);
+}
+
+template <bool ADAPT>
 __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts) {
   const QuantTensor &T = args.t[blockIdx.y];
   const float g = block_global_scale(T, nparts);
-  const BlockScaler bsc(g);
+  const BlockScaler b6(g, kE2M1Max), b4(g, 4.0f);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     *T.gscale = g;
     if (blockIdx.y == 0 && args.mark.chunk_start != nullptr) {
@@ -209,8 +276,8 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
     uint32_t b0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     uint32_t b1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
     uint32_t c0, c1, c2, c3;
-    const uint32_t s0 = encode_block16(b0, absmax16(b0), bsc, c0, c1);
-    const uint32_t s1 = encode_block16(b1, absmax16(b1), bsc, c2, c3);
+    const uint32_t s0 = encode_any<ADAPT>(b0, absmax16(b0), b6, b4, c0, c1);
+    const uint32_t s1 = encode_any<ADAPT>(b1, absmax16(b1), b6, b4, c2, c3);
     reinterpret_cast<u32x4 *>(T.codes)[u] = u32x4{c0, c1, c2, c3};
     T.scales[u] = (uint16_t)(s0 | (s1 << 8));
   }
@@ -268,7 +335,7 @@ constexpr int kResThreads = 1024;            // one workgroup per CU
 // is bounded: if it expires (the grid was not resident all at once), the
 // workgroup reads the whole tensor itself, which yields the same A, so the
 // result never depends on scheduling.
-template <int NJ, int UMAX>
+template <int NJ, int UMAX, bool ADAPT>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, uint64_t epoch,
                                                                 int u) {
   constexpr int NW = kResThreads / 64;
@@ -350,7 +417,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, 
     const QuantTensor &T = args.t[j];
     const uint32_t Abits = shared_A[j];
     const float g = (Abits == 0) ? 1.0f : bf16_bits_to_f32(Abits) / kGlobalDivisor;
-    const BlockScaler bsc(g);
+    const BlockScaler b6(g, kE2M1Max), b4(g, 4.0f);
     if (k == 0 && threadIdx.x == 0) {
       *T.gscale = g;
       if (j == 0 && args.mark.chunk_start != nullptr) {
@@ -364,7 +431,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, 
     for (int i = 0; i < UMAX; ++i) {
       const int64_t b = ((int64_t)k * u + i) * kResThreads + threadIdx.x;
       uint32_t lo, hi;
-      const uint32_t S = encode_block16(w[j][i], bm[j][i], bsc, lo, hi);
+      const uint32_t S = encode_any<ADAPT>(w[j][i], bm[j][i], b6, b4, lo, hi);
       if (i < u && b < 2 * T.units) {
         codes[b] = u32x2{lo, hi};
         scales[b] = (uint8_t)S;
@@ -377,12 +444,12 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, 
 // instance fits one workgroup per CU.
 struct ResidentLimits {
   int cus = 0;
-  bool fits[2][4] = {};                   // [NJ - 1][log2 UMAX]
+  bool fits[2][2][4] = {};                // [ADAPT][NJ - 1][log2 UMAX]
 };
 
-template <int NJ, int UMAX>
+template <int NJ, int UMAX, bool ADAPT>
 static const void *resident_fn() {
-  return reinterpret_cast<const void *>(&k_quant_resident<NJ, UMAX>);
+  return reinterpret_cast<const void *>(&k_quant_resident<NJ, UMAX, ADAPT>);
 }
 
 static const ResidentLimits &resident_limits() {
@@ -395,17 +462,22 @@ static const ResidentLimits &resident_limits() {
   if (!filled[dev]) {
     ResidentLimits &r = table[dev];
     if (hipDeviceGetAttribute(&r.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) r.cus = 0;
-    const void *fns[2][4] = {
-        {resident_fn<1, 1>(), resident_fn<1, 2>(), resident_fn<1, 4>(), resident_fn<1, 8>()},
-        {resident_fn<2, 1>(), resident_fn<2, 2>(), resident_fn<2, 4>(), nullptr}};
-    for (int j = 0; j < 2; ++j)
-      for (int i = 0; i < 4; ++i) {
-        int n = 0;
-        r.fits[j][i] = fns[j][i] != nullptr &&
-                       hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fns[j][i], kResThreads, 0) ==
-                           hipSuccess &&
-                       n >= 1;
-      }
+    const void *fns[2][2][4] = {
+        {{resident_fn<1, 1, false>(), resident_fn<1, 2, false>(), resident_fn<1, 4, false>(),
+          resident_fn<1, 8, false>()},
+         {resident_fn<2, 1, false>(), resident_fn<2, 2, false>(), resident_fn<2, 4, false>(), nullptr}},
+        {{resident_fn<1, 1, true>(), resident_fn<1, 2, true>(), resident_fn<1, 4, true>(),
+          resident_fn<1, 8, true>()},
+         {resident_fn<2, 1, true>(), resident_fn<2, 2, true>(), resident_fn<2, 4, true>(), nullptr}}};
+    for (int a = 0; a < 2; ++a)
+      for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 4; ++i) {
+          int n = 0;
+          r.fits[a][j][i] = fns[a][j][i] != nullptr &&
+                            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fns[a][j][i], kResThreads,
+                                                                         0) == hipSuccess &&
+                            n >= 1;
+        }
     filled[dev] = true;
   }
   return table[dev];
@@ -422,6 +494,7 @@ static uint64_t next_epoch() {
 
 // Launches the resident quantiser (at most one workgroup per CU) when the
 // tensors fit in its registers; returns false (nothing launched) otherwise.
+template <bool ADAPT>
 static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStream_t stream,
                             hipError_t *err) {
   const ResidentLimits &lim = resident_limits();
@@ -433,22 +506,22 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
   const int64_t u = (nb + nwg * kResThreads - 1) / (nwg * kResThreads);
   int li = 0;
   while (li < 4 && (1 << li) < u) ++li;
-  if (li == 4 || !lim.fits[njobs - 1][li]) return false;
+  if (li == 4 || !lim.fits[ADAPT][njobs - 1][li]) return false;
   const uint64_t epoch = next_epoch();
   const dim3 grid((unsigned)nwg), block(kResThreads);
   const int ui = (int)u;
   if (njobs == 1) {
     switch (li) {
-      case 0: hipLaunchKernelGGL((k_quant_resident<1, 1>), grid, block, 0, stream, a, epoch, ui); break;
-      case 1: hipLaunchKernelGGL((k_quant_resident<1, 2>), grid, block, 0, stream, a, epoch, ui); break;
-      case 2: hipLaunchKernelGGL((k_quant_resident<1, 4>), grid, block, 0, stream, a, epoch, ui); break;
-      default: hipLaunchKernelGGL((k_quant_resident<1, 8>), grid, block, 0, stream, a, epoch, ui); break;
+      case 0: hipLaunchKernelGGL((k_quant_resident<1, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<1, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
+      case 2: hipLaunchKernelGGL((k_quant_resident<1, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
+      default: hipLaunchKernelGGL((k_quant_resident<1, 8, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
     }
   } else {
     switch (li) {
-      case 0: hipLaunchKernelGGL((k_quant_resident<2, 1>), grid, block, 0, stream, a, epoch, ui); break;
-      case 1: hipLaunchKernelGGL((k_quant_resident<2, 2>), grid, block, 0, stream, a, epoch, ui); break;
-      default: hipLaunchKernelGGL((k_quant_resident<2, 4>), grid, block, 0, stream, a, epoch, ui); break;
+      case 0: hipLaunchKernelGGL((k_quant_resident<2, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<2, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
+      default: hipLaunchKernelGGL((k_quant_resident<2, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
     }
   }
   *err = hipGetLastError();
@@ -472,7 +545,7 @@ static int encode_blocks(int64_t units) {
 }
 
 hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
-                           const ChunkMark *mark) {
+                           const ChunkMark *mark, bool adaptive46) {
   QuantArgs a{};
   if (mark) a.mark = *mark;
   int64_t max_units = 0;
@@ -488,15 +561,21 @@ hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
     if (a.t[i].units > max_units) max_units = a.t[i].units;
   }
   hipError_t e = hipSuccess;
-  if (launch_resident(a, njobs, max_units, stream, &e)) return e;
+  if (adaptive46 ? launch_resident<true>(a, njobs, max_units, stream, &e)
+                 : launch_resident<false>(a, njobs, max_units, stream, &e))
+    return e;
   // Both tensors of a pair use the same grid; a tensor with fewer units simply
   // leaves some threads idle.
   const int nparts = amax_blocks(max_units);
   hipLaunchKernelGGL(k_amax, dim3(nparts, njobs), dim3(kThreads), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_encode, dim3(encode_blocks(max_units), njobs), dim3(kThreads), 0, stream, a,
-                     nparts);
+  if (adaptive46)
+    hipLaunchKernelGGL(k_encode<true>, dim3(encode_blocks(max_units), njobs), dim3(kThreads), 0, stream,
+                       a, nparts);
+  else
+    hipLaunchKernelGGL(k_encode<false>, dim3(encode_blocks(max_units), njobs), dim3(kThreads), 0, stream,
+                       a, nparts);
   return hipGetLastError();
 }
 

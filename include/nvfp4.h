@@ -62,6 +62,12 @@ extern "C" {
 #define NVFP4_TILE_128x256  0x500u
 #define NVFP4_TILE_128x128  0x600u
 
+/* flags for nvfp4_quantize_ex / nvfp4_kv_append_ex */
+/* Adaptive {4, 6} block scales: each 16-block is encoded with its amax mapped
+ * to 6 and to 4 and the encoding with the smaller binary32 squared error is
+ * kept (ties to 6).  The output format is unchanged. */
+#define NVFP4_Q_ADAPTIVE_4_6 0x10u
+
 /* Alignment every device pointer must satisfy (bytes). */
 #define NVFP4_ALIGN 16
 
@@ -91,6 +97,21 @@ int nvfp4_quantize_workspace(int64_t M, int64_t K, size_t *bytes);
 int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K,
                    uint8_t *codes, uint8_t *scales, float *gscale,
                    void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * nvfp4_quantize with quantiser flags (0 or NVFP4_Q_ADAPTIVE_4_6).
+ * Source of the adaptive mode: 二、方法 / 推理底座 (adaptive scale selection for
+ * the KV chunks) and the distillation paragraph of 二、方法 (amax targets
+ * {4, 6}).  With the flag, each 16-block is encoded twice: as above, and with
+ * the divisor 4g in place of 6g (S4 = E4M3_rne_satfinite(a/(4g)),
+ * r4 = 1/(S4·g)).  For each encoding err = Σ_i fl(e_i·e_i) accumulated in
+ * binary32 in element order, e_i = fl(x_i − fl(fl(E2M1_i·S)·g)) with the
+ * code's sign; the amax→4 encoding is kept only when its err is smaller.
+ * Returns NVFP4_EINVAL for unknown flags; other arguments as nvfp4_quantize.
+ */
+int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags,
+                      uint8_t *codes, uint8_t *scales, float *gscale,
+                      void *ws, size_t ws_bytes, void *stream);
 
 /*
  * W4A4 GEMM with FP32 accumulation and a bf16 epilogue:
@@ -179,6 +200,15 @@ int nvfp4_kv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t
  */
 int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T,
                     int64_t ld, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * nvfp4_kv_append with quantiser flags (0 or NVFP4_Q_ADAPTIVE_4_6, as for
+ * nvfp4_quantize_ex; 二、方法 / 推理底座 selects adaptive scales for the KV
+ * chunks).  The flag may differ between appends: dequantisation reads every
+ * chunk the same way.  Returns NVFP4_EINVAL for unknown flags.
+ */
+int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T,
+                       int64_t ld, uint32_t qflags, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Dequantise tokens [t0, t1) of K and V to bf16 [t1-t0, heads, head_dim]:

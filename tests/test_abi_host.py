@@ -177,3 +177,14 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         nv.quantize(x)
+
+
+def test_quantizer_flags_rejected(L):
+    # unknown quantiser flags are argument errors, found before any launch
+    assert L.nvfp4_quantize_ex(FAKE, 64, 64, 0x20, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    assert L.nvfp4_quantize_ex(FAKE, 64, 64, 0x1, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    d = _lib.KVCacheDesc(100, 24, 128, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)
+    assert L.nvfp4_kv_init(C.byref(d)) == 0
+    assert L.nvfp4_kv_append_ex(C.byref(d), FAKE, FAKE, 1, 3072, 0x30, FAKE, 1 << 20, None) == EINVAL
+    assert d.n_tokens == 0 and d.n_chunks == 0
+    assert b"flags" in L.nvfp4_last_error()
