@@ -339,6 +339,18 @@ def _time_events(torch, fn, reps, flush=None):
     return ts
 
 
+def _dequant_rel_err(torch, x, codes, scales, g):
+    """‖x − Dequant(q)‖ / ‖x‖ in fp32 (a reported statistic, computed with torch)."""
+    e2m1 = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6],
+                        dtype=torch.float32, device=x.device)
+    lo, hi = (codes & 15).long(), (codes >> 4).long()
+    vals = torch.stack((e2m1[lo], e2m1[hi]), dim=-1).reshape(codes.shape[0], -1)
+    s = scales.view(torch.float8_e4m3fn).float().repeat_interleave(16, dim=1)
+    d = vals * s * g.float()
+    xf = x.float()
+    return float(torch.linalg.vector_norm(xf - d) / torch.linalg.vector_norm(xf))
+
+
 def extended(path, nv, torch, np, workloads, dev, up):
     """Per-kernel numbers on the other DiT shapes and the full KV sequence."""
     lines = []
@@ -363,6 +375,23 @@ def extended(path, nv, torch, np, workloads, dev, up):
         lines.append({"shape": name, "M": M, "N": N, "K": K, "gemm_us": tg,
                       "gemm_tflops": 2 * M * N * K / tg / 1e6, "tile": nv.gemm_tile(M, N, K),
                       "quantize_us_cold": tq, "quantize_gbs_cold": qb / tq / 1e3})
+        if name == "qkv":
+            # adaptive {4, 6} block scales: time (cold) and normwise dequant error
+            # against the standard amax→6 encoding, for X and for the weights
+            for tname, t, rows in (("X", x, M), ("W", W, N)):
+                ws_t = torch.empty((nv.quantize_workspace_bytes(rows, K),), dtype=torch.uint8, device=dev)
+                oc = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
+                os_ = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
+                og = torch.empty((1,), dtype=torch.float32, device=dev)
+                rec = {"shape": f"qkv_{tname}_adaptive46", "rows": rows, "K": K}
+                for mode, ad in (("std", False), ("adaptive", True)):
+                    f = lambda: nv.quantize_into(t, oc, os_, og, ws_t, adaptive46=ad)
+                    tt = float(np.median(_time_events(torch, f, 10, flush)))
+                    f(); torch.cuda.synchronize()
+                    rec[f"{mode}_us_cold"] = tt
+                    rec[f"{mode}_gbs_cold"] = rows * K * 2.5625 / tt / 1e3
+                    rec[f"{mode}_rel_err"] = _dequant_rel_err(torch, t, oc, os_, og)
+                lines.append(rec)
         if name == "ffn_up":
             # down projection: H = GELU output (bf16 [8192, 14336]) quantised, times W_down
             Wd = up(w.w2)
@@ -395,6 +424,15 @@ def extended(path, nv, torch, np, workloads, dev, up):
 
     seq(); torch.cuda.synchronize()
     tseq = float(np.median(_time_events(torch, seq, 5, flush)))
+
+    def seq46():
+        cache.reset()
+        for i in range(len(sizes)):
+            cache.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]], adaptive46=True)
+
+    seq46(); torch.cuda.synchronize()
+    tseq46 = float(np.median(_time_events(torch, seq46, 5, flush)))
+    seq(); torch.cuda.synchronize()
     ko = torch.empty((T, 24, 128), dtype=torch.bfloat16, device=dev)
     vo = torch.empty_like(ko)
     deq = lambda: cache.dequant(0, T, ko, vo)
@@ -402,6 +440,7 @@ def extended(path, nv, torch, np, workloads, dev, up):
     kvb = 2 * T * 3072 * 2.5625
     lines.append({"shape": "kv_65536", "appends": len(sizes), "append_seq_us": tseq,
                   "append_seq_gbs": kvb / tseq / 1e3, "append_us_per_chunk": tseq / len(sizes),
+                  "append_seq_adaptive46_us": tseq46,
                   "dequant_us": tdq, "dequant_gbs": kvb / tdq / 1e3})
     with open(path, "w") as f:
         for l in lines:

@@ -1,0 +1,111 @@
+"""GPU parity of the DiT FFN chain: up projection with the GELU epilogue, NVFP4
+quantisation of the hidden activation H, down projection.
+
+The chain is checked stage by stage.  Each GPU stage takes the oracle's own
+intermediate as its input (never the reverse), so every expected value comes
+from the oracle alone.  A GPU H that differs from the oracle's H in the last
+bf16 bit (GELU's exponential is evaluated differently on the two sides) may
+change a few codes downstream, so the end-to-end GPU chain is compared with a
+looser normwise bound.  The full-size up and down projections are checked on
+sampled rows and columns.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_amd as nv
+import oracle
+import workloads
+from gpu_helpers import (GEMM_TOL, announce, bf16_to_dev, f32_to_dev, gemm_errors, to_bits, to_np,
+                         u8_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+CHAIN_TOL = 2e-2          # end to end, GPU intermediates throughout
+
+
+def _upload_q(q):
+    c, s, g = q
+    return u8_to_dev(c), u8_to_dev(s), f32_to_dev(g)
+
+
+def test_ffn_chain_stagewise():
+    M, D, HID = 256, 512, 2048
+    announce(f"ffn chain M={M} D={D} hidden={HID}")
+    x = workloads.random_matrix(21, M, D, 1.0, outliers=True)
+    w_up = workloads.random_matrix(22, HID, D, 0.02)
+    w_dn = workloads.random_matrix(23, D, HID, 0.02)
+    qx, qu, qd = oracle.quantize(x), oracle.quantize(w_up), oracle.quantize(w_dn)
+    h64, h_ref = oracle.gemm_ref(*qx, *qu, gelu=True)
+    qh = oracle.quantize(h_ref)
+    y64, y_ref = oracle.gemm_ref(*qh, *qd)
+
+    # stage 1: linear (GPU quantiser + GEMM + GELU) on the seeded input
+    h_gpu = nv.linear(bf16_to_dev(x), *_upload_q(qu), gelu=True)
+    torch.cuda.synchronize()
+    e_ref, e_64 = gemm_errors(to_bits(h_gpu), h64, h_ref)
+    announce(f"  up+GELU: {e_ref:.3e} vs bf16 oracle, {e_64:.3e} vs fp64")
+    assert e_ref <= GEMM_TOL and e_64 <= GEMM_TOL
+
+    # stage 2: quantise the oracle's H on the GPU, bit-exact
+    c, s, g = nv.quantize(bf16_to_dev(h_ref))
+    torch.cuda.synchronize()
+    assert to_np(g)[0] == qh[2]
+    assert np.array_equal(to_np(s), qh[1]) and np.array_equal(to_np(c), qh[0])
+
+    # stage 3: down projection on the oracle's quantised H
+    y_gpu = nv.gemm(*_upload_q(qh), *_upload_q(qd))
+    torch.cuda.synchronize()
+    e_ref, e_64 = gemm_errors(to_bits(y_gpu), y64, y_ref)
+    announce(f"  down: {e_ref:.3e} vs bf16 oracle, {e_64:.3e} vs fp64")
+    assert e_ref <= GEMM_TOL and e_64 <= GEMM_TOL
+
+    # end to end on the GPU's own intermediates and its own weight quantisation
+    wu_q = nv.quantize(bf16_to_dev(w_up))
+    wd_q = nv.quantize(bf16_to_dev(w_dn))
+    h = nv.linear(bf16_to_dev(x), *wu_q, gelu=True)
+    y = nv.linear(h, *wd_q)
+    torch.cuda.synchronize()
+    yb = oracle.bf16_bits_to_f32(to_bits(y)).astype(np.float64)
+    err = np.linalg.norm(yb - y64) / np.linalg.norm(y64)
+    announce(f"  end to end: {err:.3e} vs fp64 chain")
+    assert err <= CHAIN_TOL
+
+
+def _sampled(x_bits, w_bits, rows, cols, gelu):
+    """GPU linear on the full shape; oracle on sampled rows x columns."""
+    qw = oracle.quantize(w_bits)
+    out = nv.linear(bf16_to_dev(x_bits), *_upload_q(qw), gelu=gelu)
+    torch.cuda.synchronize()
+    A = np.abs(oracle.bf16_bits_to_f32(x_bits)).max()
+    qa = oracle.quantize(x_bits[rows], amax=A)
+    c64, cref = oracle.gemm_ref(*qa, qw[0][cols], qw[1][cols], qw[2], gelu=gelu)
+    return gemm_errors(to_bits(out)[np.ix_(rows, cols)], c64, cref)
+
+
+def test_ffn_up_full_size_sampled():
+    w = workloads.ffn()
+    announce("ffn up 8192x14336x3072 + GELU (sampled check)")
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.r_[0:32, rng.integers(0, w.M, 64), w.M - 32:w.M])
+    cols = np.unique(np.r_[0:64, rng.integers(0, w.N, 256), w.N - 64:w.N])
+    e_ref, e_64 = _sampled(w.x, w.w, rows, cols, gelu=True)
+    announce(f"  normwise err vs bf16 oracle {e_ref:.3e}, vs fp64 {e_64:.3e}")
+    assert e_ref <= GEMM_TOL and e_64 <= GEMM_TOL
+
+
+def test_ffn_down_full_size_sampled():
+    # the down projection at its full shape, on a GELU-like synthetic H
+    w = workloads.ffn()
+    rng = np.random.default_rng(24)
+    h = rng.standard_normal((w.M, w.N), dtype=np.float32) * 0.7
+    h = np.where(h > 0, h, 0.05 * h).astype(np.float32)
+    hb = workloads.to_bf16_bits(h)
+    del h
+    announce("ffn down 8192x3072x14336 (sampled check)")
+    rows = np.unique(np.r_[0:32, rng.integers(0, w.M, 64), w.M - 32:w.M])
+    cols = np.unique(np.r_[0:64, rng.integers(0, w.K, 192), w.K - 64:w.K])
+    e_ref, e_64 = _sampled(hb, w.w2, rows, cols, gelu=False)
+    announce(f"  normwise err vs bf16 oracle {e_ref:.3e}, vs fp64 {e_64:.3e}")
+    assert e_ref <= GEMM_TOL and e_64 <= GEMM_TOL
