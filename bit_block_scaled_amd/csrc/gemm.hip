@@ -228,40 +228,57 @@ __device__ __forceinline__ void interleave_hint() {
   }
 }
 
-template <int WM, int WN, bool KTAIL>
+// PERSIST: the workgroup loops over tiles w, w + grid, ... and prefetches the
+// next tile's first stage under the current epilogue; otherwise one tile per
+// workgroup (the 256x256 tile has no registers left for the loop state).
+template <int WM, int WN, bool KTAIL, bool PERSIST>
 __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_m, int tiles_n) {
   using T = Tile<WM, WN>;
   constexpr int BM = T::BM, BN = T::BN, NQ = WM + WN;
   __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
 
-  // tile order: contiguous runs of tiles per XCD (workgroups are dealt to the
-  // 8 XCDs round-robin), M-fastest inside groups of 8 M-tiles so concurrently
-  // running tiles share weight rows in L2.
-  int b = blockIdx.x;
   const int ntiles = tiles_m * tiles_n;
-  if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
-  constexpr int GM = 8;
-  const int per_group = GM * tiles_n;
-  const int grp = b / per_group, first_m = grp * GM;
-  const int gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
-  const int in = b - grp * per_group;
-  const int tile_m = first_m + in % gsz, tile_n = in / gsz;
-
-  const int64_t m0 = (int64_t)tile_m * BM, n0 = (int64_t)tile_n * BN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int r = lane & 31, h = lane >> 5;
   const int nk = (int)((a.K + kBK - 1) / kBK);
   const int64_t rb = a.K / 2, sbytes = a.K / 16;
 
-  // rows past the matrix end are outside the buffer ranges and read as 0;
-  // their results are not stored
-  const int64_t rows_a = (a.M - m0) < BM ? (a.M - m0) : BM;
-  const int64_t rows_w = (a.N - n0) < BN ? (a.N - n0) : BN;
-  const Operand opa{a.Aq + m0 * rb, a.As + m0 * sbytes, (uint32_t)(rows_a * rb), (uint32_t)(rows_a * sbytes)};
-  const Operand opw{a.Wq + n0 * rb, a.Ws + n0 * sbytes, (uint32_t)(rows_w * rb), (uint32_t)(rows_w * sbytes)};
+  // Tile t → (m0, n0): contiguous runs of tiles per XCD (workgroup w runs on
+  // XCD w % 8 and processes tiles w, w + grid, ... with grid a multiple of 8,
+  // so every tile it gets maps to its own XCD's run), M-fastest inside groups
+  // of 8 M-tiles so concurrently running tiles share weight rows in L2.
+  // Rows past the matrix end are outside the buffer ranges and read as 0;
+  // their results are not stored.
+  int64_t m0 = 0, n0 = 0;
+  Operand opa, opw;
+  auto setup = [&](int t) {
+    int b = t;
+    if ((ntiles & 7) == 0 && (gridDim.x & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
+    constexpr int GM = 8;
+    const int per_group = GM * tiles_n;
+    const int grp = b / per_group, first_m = grp * GM;
+    const int gsz = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+    const int in = b - grp * per_group;
+    m0 = (int64_t)(first_m + in % gsz) * BM;
+    n0 = (int64_t)(in / gsz) * BN;
+    const int64_t rows_a = (a.M - m0) < BM ? (a.M - m0) : BM;
+    const int64_t rows_w = (a.N - n0) < BN ? (a.N - n0) : BN;
+    opa = Operand{a.Aq + m0 * rb, a.As + m0 * sbytes, (uint32_t)(rows_a * rb), (uint32_t)(rows_a * sbytes)};
+    opw = Operand{a.Wq + n0 * rb, a.Ws + n0 * sbytes, (uint32_t)(rows_w * rb), (uint32_t)(rows_w * sbytes)};
+  };
 
   f32x16 acc[WN][WM];
+  Fill<BM> fa;
+  Fill<BN> fw;
+  Frag<NQ> fr;
+  f16x8 f0[NQ], f1[NQ];
+
+  int t = blockIdx.x;
+  setup(t);
+  fill_load<BM, KTAIL>(fa, opa, a.K, 0);
+  fill_load<BN, KTAIL>(fw, opw, a.K, 0);
+  for (;;) {
 #pragma unroll
   for (int j = 0; j < WN; ++j)
 #pragma unroll
@@ -269,19 +286,14 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[j][i][v] = 0.0f;
 
-  Fill<BM> fa;
-  Fill<BN> fw;
-  // prologue: stage 0 into LDS buffer 0, stage 1 in flight in registers
-  fill_load<BM, KTAIL>(fa, opa, a.K, 0);
-  fill_load<BN, KTAIL>(fw, opw, a.K, 0);
+  // prologue: stage 0 (already in registers) into LDS buffer 0, stage 1 in
+  // flight in registers
   fill_store<BM>(fa, smem + T::A_CODE, smem + T::A_SCALE);
   fill_store<BN>(fw, smem + T::W_CODE, smem + T::W_SCALE);
   fill_load<BM, KTAIL>(fa, opa, a.K, 1);
   fill_load<BN, KTAIL>(fw, opw, a.K, 1);
   __syncthreads();
 
-  Frag<NQ> fr;
-  f16x8 f0[NQ], f1[NQ];
   frag_read<WM, WN>(fr, smem, wm, wn, r, h);
   decode_step<0, NQ>(fr, h, f0);
 
@@ -308,6 +320,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
     decode_step<0, NQ>(fr, h, f0); mfma_step<WM, WN>(acc, f1); interleave_hint<WM, WN, 7>();
   }
 
+  // the next tile's first stage is fetched now, so its latency hides behind
+  // this tile's epilogue
+  const int64_t cm0 = m0, cn0 = n0;
+  const int t_next = PERSIST ? t + (int)gridDim.x : ntiles;
+  if (PERSIST && t_next < ntiles) {
+    setup(t_next);
+    fill_load<BM, KTAIL>(fa, opa, a.K, 0);
+    fill_load<BN, KTAIL>(fw, opw, a.K, 0);
+  }
+
   // ---- epilogue: acc[j][i][v] is C[m][n] with m = (row block i) + r,
   //      n = (column block j) + 8·(v/4) + 4·h + v%4.  Each operation rounds on
   //      its own (no fused multiply-add), as the interface states.  Each row
@@ -319,8 +341,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
     constexpr int PITCH = 64 * WN + 16;  // bytes per staged row (32·WN bf16 + pad)
     constexpr int CPR = 4 * WN;          // 16-byte chunks per staged row
     uint8_t *wreg = smem + wave * 32 * PITCH;
-    const int64_t mw = m0 + wm * 32 * WM, nw = n0 + wn * 32 * WN;
-    const bool full = (m0 + BM <= a.M) && (n0 + BN <= a.N) && ((a.N & 7) == 0);
+    const int64_t mw = cm0 + wm * 32 * WM, nw = cn0 + wn * 32 * WN;
+    const bool full = (cm0 + BM <= a.M) && (cn0 + BN <= a.N) && ((a.N & 7) == 0);
     const float gg = a.Ag[0] * a.Wg[0];
     const bool gelu = (a.flags & NVFP4_EPI_GELU_TANH) != 0;
     const bool has_bias = a.bias != nullptr;
@@ -383,6 +405,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
       }
     }
   }
+  if (t_next >= ntiles) break;
+  t = t_next;
+  __syncthreads();                       // the staged epilogue is read before the next fills
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -418,14 +444,32 @@ void gemm_tile_for(int64_t M, int64_t N, int64_t, int *bm, int *bn) {
   *bn = 64 * c.wn;
 }
 
+static int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Persistent launch: one workgroup per CU (the LDS ring and the registers
+// allow no more), each looping over tiles w, w + grid, ...
 template <int WM, int WN>
 static hipError_t launch_t(const GemmArgs &a, hipStream_t stream) {
   constexpr int BM = 64 * WM, BN = 64 * WN;
+  constexpr bool P = !(WM == 4 && WN == 4);
   const int tm = (int)((a.M + BM - 1) / BM), tn = (int)((a.N + BN - 1) / BN);
+  const int ntiles = tm * tn;
+  const int cus = device_cus();
+  const int grid = (P && ntiles > cus) ? cus : ntiles;
   if (a.K % kBK == 0)
-    hipLaunchKernelGGL((k_gemm<WM, WN, false>), dim3(tm * tn), dim3(kGemmThreads), 0, stream, a, tm, tn);
+    hipLaunchKernelGGL((k_gemm<WM, WN, false, P>), dim3(grid), dim3(kGemmThreads), 0, stream, a, tm, tn);
   else
-    hipLaunchKernelGGL((k_gemm<WM, WN, true>), dim3(tm * tn), dim3(kGemmThreads), 0, stream, a, tm, tn);
+    hipLaunchKernelGGL((k_gemm<WM, WN, true, P>), dim3(grid), dim3(kGemmThreads), 0, stream, a, tm, tn);
   return hipGetLastError();
 }
 
