@@ -407,6 +407,27 @@ def extended(path, nv, torch, np, workloads, dev, up):
             lines.append({"shape": "ffn_down", "M": M, "N": K, "K": N, "gemm_us": td,
                           "gemm_tflops": 2 * M * N * K / td / 1e6, "tile": nv.gemm_tile(M, K, N),
                           "quantize_us_cold": tqh, "quantize_gbs_cold": M * N * 2.5625 / tqh / 1e3})
+            # the whole FFN: linear(up, GELU) → quantise H → down GEMM, against
+            # linear_q (H's maxima from the up GEMM's epilogue, H read once)
+            lws = torch.empty((nv.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+            qws_ = torch.empty((nv.linear_q_workspace_bytes(M, N, K),), dtype=torch.uint8, device=dev)
+
+            def chain():
+                nv.linear(x, wq, wsc, wg, gelu=True, out=C, ws=lws)
+                nv.quantize_into(C, hq, hsc, hg, hws)
+                nv.gemm(hq, hsc, hg, dq, dsc, dg, out=Cd)
+
+            def chain_q():
+                nv.linear_q(x, wq, wsc, wg, gelu=True, out=(hq, hsc, hg), ws=qws_)
+                nv.gemm(hq, hsc, hg, dq, dsc, dg, out=Cd)
+            chain(); chain_q(); torch.cuda.synchronize()
+            tc = float(np.median(_time_events(torch, chain, 10, flush)))
+            tcq = float(np.median(_time_events(torch, chain_q, 10, flush)))
+            flops_ffn = 4.0 * M * N * K
+            lines.append({"shape": "ffn_chain", "M": M, "D": K, "hidden": N,
+                          "linear_quantize_gemm_us": tc, "linear_q_gemm_us": tcq,
+                          "tflops_unfused": flops_ffn / tc / 1e6, "tflops_linear_q": flops_ffn / tcq / 1e6})
+            del qws_, lws
         del x, W, C
         torch.cuda.empty_cache()
     # the 65536-token KV sequence: 74 appends of 880 tokens + one of 416, then a full dequant

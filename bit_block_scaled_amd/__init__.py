@@ -28,8 +28,8 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-__all__ = ["quantize", "quantize_into", "gemm", "linear", "KVCache", "NVFP4Error", "lib",
-           "gemm_tile", "quantize_workspace_bytes", "linear_workspace_bytes"]
+__all__ = ["quantize", "quantize_into", "gemm", "linear", "linear_q", "KVCache", "NVFP4Error", "lib",
+           "gemm_tile", "quantize_workspace_bytes", "linear_workspace_bytes", "linear_q_workspace_bytes"]
 
 
 def _stream(device=None):
@@ -147,6 +147,41 @@ def linear(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, ws=None, tile=None):
     check(lib().nvfp4_linear(_ptr(x), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias), _ptr(out),
                              M, N, K, flags, _ptr(ws), ws.numel(), _stream(x.device)))
     return out
+
+
+def linear_q_workspace_bytes(M: int, N: int, K: int) -> int:
+    n = C.c_size_t()
+    check(lib().nvfp4_linear_q_workspace(M, N, K, C.byref(n)))
+    return n.value
+
+
+def linear_q(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, ws=None, tile=None):
+    """nvfp4_linear_q: the linear layer's bf16 output handed on in NVFP4.
+    Returns (Hq u8 [M, N/2], Hs u8 [M, N/16], Hg f32 [1]); ``out`` may pass
+    that triple to write into."""
+    M, K = x.shape
+    N = Wq.shape[0]
+    _need(x, torch.bfloat16, "x")
+    _need(Wq, torch.uint8, "Wq", (N, K // 2))
+    _need(Ws, torch.uint8, "Ws", (N, K // 16))
+    _need(Wg, torch.float32, "Wg", (1,))
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", (N,))
+    if out is None:
+        out = (torch.empty((M, N // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((M, N // 16), dtype=torch.uint8, device=x.device),
+               torch.empty((1,), dtype=torch.float32, device=x.device))
+    Hq, Hs, Hg = out
+    _need(Hq, torch.uint8, "Hq", (M, N // 2))
+    _need(Hs, torch.uint8, "Hs", (M, N // 16))
+    _need(Hg, torch.float32, "Hg", (1,))
+    if ws is None:
+        ws = torch.empty((linear_q_workspace_bytes(M, N, K),), dtype=torch.uint8, device=x.device)
+    _need(ws, torch.uint8, "ws")
+    flags = _flags(gelu, tile)
+    check(lib().nvfp4_linear_q(_ptr(x), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias), M, N, K, flags,
+                               _ptr(Hq), _ptr(Hs), _ptr(Hg), _ptr(ws), ws.numel(), _stream(x.device)))
+    return Hq, Hs, Hg
 
 
 class KVCache:

@@ -49,6 +49,9 @@ _SIGS = {
     "nvfp4_gemm_tile": ([_i64, _i64, _i64, C.POINTER(C.c_int), C.POINTER(C.c_int)], C.c_int),
     "nvfp4_linear_workspace": ([_i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_linear": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, C.c_uint32, _p, _sz, _p], C.c_int),
+    "nvfp4_linear_q_workspace": ([_i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
+    "nvfp4_linear_q": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, C.c_uint32, _p, _p, _p, _p, _sz, _p],
+                       C.c_int),
     "nvfp4_kv_init": ([C.POINTER(KVCacheDesc)], C.c_int),
     "nvfp4_kv_append_workspace": ([_i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_kv_append": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _i64, _p, _sz, _p], C.c_int),

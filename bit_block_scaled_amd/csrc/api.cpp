@@ -165,6 +165,66 @@ int nvfp4_linear(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const 
   return hip_status(nvfp4::launch_gemm(a, st), "linear/gemm");
 }
 
+// nvfp4_linear_q workspace: [linear workspace | tile maxima | H bf16 [M, N]]
+struct LinearQWs {
+  LinearWs lin;
+  size_t slots, h, total;
+  int64_t max_tiles;
+};
+
+static LinearQWs linear_q_ws(int64_t M, int64_t N, int64_t K) {
+  LinearQWs w;
+  w.lin = linear_ws(M, K);
+  w.max_tiles = ((M + 127) / 128) * ((N + 127) / 128);   // the finest tiling the GEMM uses
+  w.slots = w.lin.total;
+  w.h = round_up(w.slots + size_t(w.max_tiles) * sizeof(uint32_t), 256);
+  w.total = round_up(w.h + size_t(M) * size_t(N) * sizeof(uint16_t), 256);
+  return w;
+}
+
+int nvfp4_linear_q_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes) {
+  if (bytes == nullptr) return fail(NVFP4_EINVAL, "bytes is NULL");
+  int s = check_mk(M, K, "linear_q_workspace");
+  if (s) return s;
+  if (N < 32 || N % 32) return fail(NVFP4_EINVAL, "linear_q_workspace: N must be a positive multiple of 32");
+  if (N > kMaxElements / K || M > kMaxElements / N) return fail(NVFP4_EINVAL, "linear_q_workspace: problem too large");
+  *bytes = linear_q_ws(M, N, K).total;
+  return NVFP4_OK;
+}
+
+int nvfp4_linear_q(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const float *Wg,
+                   const uint16_t *bias, int64_t M, int64_t N, int64_t K, uint32_t flags, uint8_t *Hq,
+                   uint8_t *Hs, float *Hg, void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if (N < 32 || N % 32) return fail(NVFP4_EINVAL, "linear_q: N must be a positive multiple of 32");
+  if ((s = check_mk(M, K, "linear_q"))) return s;
+  if (N > kMaxElements / K || M > kMaxElements / N) return fail(NVFP4_EINVAL, "linear_q: problem too large");
+  if ((s = check_ptr(ws, "ws"))) return s;
+  const LinearQWs w = linear_q_ws(M, N, K);
+  if (ws_bytes < w.total) return fail(NVFP4_EWORKSPACE, "linear_q: workspace too small");
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  uint16_t *H = reinterpret_cast<uint16_t *>(base + w.h);
+  if ((s = check_gemm_args(nullptr, nullptr, nullptr, Wq, Ws, Wg, bias, H, M, N, K, flags, false))) return s;
+  if ((s = check_ptr(x, "x"))) return s;
+  if ((s = check_ptr(Hq, "Hq"))) return s;
+  if ((s = check_ptr(Hs, "Hs"))) return s;
+  if ((s = check_ptr(Hg, "Hg", 4))) return s;
+  uint8_t *aq = base + w.lin.codes;
+  uint8_t *as = base + w.lin.scales;
+  float *ag = reinterpret_cast<float *>(base + w.lin.gscale);
+  uint32_t *slots = reinterpret_cast<uint32_t *>(base + w.slots);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  nvfp4::QuantJob jx{x, aq, as, ag, reinterpret_cast<uint32_t *>(base + w.lin.partials), M, K, K};
+  if ((s = hip_status(nvfp4::launch_quantize(&jx, 1, st), "linear_q/quantize"))) return s;
+  nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, H, M, N, K, flags};
+  a.tile_amax = slots;
+  const int64_t tiles = nvfp4::gemm_tile_count(a);
+  if (tiles > w.max_tiles) return fail(NVFP4_EHIP, "linear_q: internal tile count exceeds the workspace");
+  if ((s = hip_status(nvfp4::launch_gemm(a, st), "linear_q/gemm"))) return s;
+  nvfp4::QuantJob jh{H, Hq, Hs, Hg, slots, M, N, N};
+  return hip_status(nvfp4::launch_encode_from_partials(jh, tiles, st), "linear_q/encode");
+}
+
 int nvfp4_kv_init(nvfp4_kv_cache *c) {
   int s;
   if (c == nullptr) return fail(NVFP4_EINVAL, "kv_init: cache is NULL");

@@ -336,6 +336,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
   //      block is staged through the wave's own LDS region so the stores are
   //      16 contiguous bytes per lane along the rows of C.
   __syncthreads();                       // every wave is done with the stage buffers
+  uint32_t tmax = 0;                     // largest stored |bf16| pattern (tile_amax)
   {
 #pragma clang fp contract(off)
     constexpr int PITCH = 64 * WN + 16;  // bytes per staged row (32·WN bf16 + pad)
@@ -366,6 +367,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
         }
       }
 
+    const bool track = a.tile_amax != nullptr;
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
 #pragma unroll
@@ -390,6 +392,21 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
         const u32x4 v = *reinterpret_cast<const u32x4 *>(wreg + row * PITCH + 16 * c);
         const int64_t m = mw + 32 * i + row, n = nw + 8 * c;
         uint16_t *dst = a.C + m * a.N + n;
+        if (track) {
+          if (full) {
+            uint32_t p = absmax_bf16x2(absmax_bf16x2(0u, v.x), v.y);
+            p = absmax_bf16x2(absmax_bf16x2(p, v.z), v.w);
+            p = (p & 0xFFFFu) > (p >> 16) ? (p & 0xFFFFu) : (p >> 16);
+            tmax = tmax > p ? tmax : p;
+          } else if (m < a.M) {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t mag = (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu;
+              if (n + e < a.N && mag > tmax) tmax = mag;
+            }
+          }
+        }
         if (full) {
           *reinterpret_cast<u32x4 *>(dst) = v;
         } else if (m < a.M) {
@@ -403,6 +420,18 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
           }
         }
       }
+    }
+  }
+  if (a.tile_amax != nullptr) {
+    __shared__ uint32_t tred[kGemmThreads / 64];
+    const uint32_t wmax = wave_max_u32(tmax);
+    if (lane == 0) tred[wave] = wmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t mx = tred[0];
+#pragma unroll
+      for (int w = 1; w < kGemmThreads / 64; ++w) mx = mx > tred[w] ? mx : tred[w];
+      a.tile_amax[t] = mx;
     }
   }
   if (t_next >= ntiles) break;
@@ -473,10 +502,20 @@ static hipError_t launch_t(const GemmArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
+static TileChoice tile_of(const GemmArgs &a) {
   static const TileChoice by_flag[] = {{0, 0}, {4, 4}, {4, 3}, {3, 4}, {4, 2}, {2, 4}, {2, 2}};
   const uint32_t tf = (a.flags & NVFP4_TILE_MASK) >> 8;
-  const TileChoice c = tf ? by_flag[tf] : choose_tile(a.M, a.N);
+  return tf ? by_flag[tf] : choose_tile(a.M, a.N);
+}
+
+int64_t gemm_tile_count(const GemmArgs &a) {
+  const TileChoice c = tile_of(a);
+  const int64_t bm = 64 * c.wm, bn = 64 * c.wn;
+  return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn);
+}
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream) {
+  const TileChoice c = tile_of(a);
   if (c.wm == 4 && c.wn == 4) return launch_t<4, 4>(a, stream);
   if (c.wm == 4 && c.wn == 3) return launch_t<4, 3>(a, stream);
   if (c.wm == 3 && c.wn == 4) return launch_t<3, 4>(a, stream);

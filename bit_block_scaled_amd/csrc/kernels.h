@@ -35,6 +35,11 @@ struct ChunkMark {
   int64_t value;
 };
 
+// Encodes one tensor in a single pass when its |x| maximum is already known as
+// the largest of `nparts` 15-bit bf16 magnitude patterns at job.partials (the
+// per-tile maxima a GEMM epilogue wrote): the same bytes as launch_quantize.
+hipError_t launch_encode_from_partials(const QuantJob &job, int64_t nparts, hipStream_t stream);
+
 // Quantises one or two tensors (njobs in {1, 2}) on `stream`: one launch when
 // the grid fits on the device at once, else two launches.
 // adaptive46 selects the adaptive {4, 6} block scales.
@@ -52,9 +57,16 @@ struct GemmArgs {
   uint16_t *C;
   int64_t M, N, K;
   uint32_t flags;
+  // optional: every workgroup tile writes the largest magnitude of its stored
+  // outputs (the 15-bit pattern of the bf16 result) to tile_amax[tile]; the
+  // array has gemm_tile_count(...) entries
+  uint32_t *tile_amax = nullptr;
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
+
+// Number of workgroup tiles launch_gemm uses for these arguments.
+int64_t gemm_tile_count(const GemmArgs &a);
 
 // Tile shape chosen for a problem (exposed for the benchmark's reporting).
 void gemm_tile_for(int64_t M, int64_t N, int64_t K, int *bm, int *bn);

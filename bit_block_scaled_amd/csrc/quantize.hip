@@ -544,6 +544,22 @@ static int encode_blocks(int64_t units) {
   return (int)b;
 }
 
+hipError_t launch_encode_from_partials(const QuantJob &job, int64_t nparts, hipStream_t stream) {
+  QuantArgs a{};
+  a.t[0].x = job.x;
+  a.t[0].codes = job.codes;
+  a.t[0].scales = reinterpret_cast<uint16_t *>(job.scales);
+  a.t[0].gscale = job.gscale;
+  a.t[0].partials = job.partials;
+  a.t[0].units = job.rows * (job.cols / 32);
+  a.t[0].units_per_row = (uint32_t)(job.cols / 32);
+  a.t[0].ld = job.ld;
+  if (nparts < 1 || nparts > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_encode<false>, dim3(encode_blocks(a.t[0].units), 1), dim3(kThreads), 0, stream, a,
+                     (int)nparts);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
                            const ChunkMark *mark, bool adaptive46) {
   QuantArgs a{};

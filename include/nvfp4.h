@@ -134,6 +134,27 @@ int nvfp4_gemm(const uint8_t *Aq, const uint8_t *As, const float *Ag,
                const uint16_t *bias, uint16_t *C,
                int64_t M, int64_t N, int64_t K, uint32_t flags, void *stream);
 
+/* Workspace bytes nvfp4_linear_q needs (includes the bf16 [M, N] output). */
+int nvfp4_linear_q_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes);
+
+/*
+ * A linear layer whose bf16 output H is handed on in NVFP4, as the input of
+ * the next W4A4 layer (the FFN up projection feeding the down projection):
+ *   H = nvfp4_linear(x, W, bias, flags);  (Hq, Hs, Hg) = nvfp4_quantize(H)
+ * with exactly those bytes.  Source: 二、方法 / 推理底座 (W4A4 inference) and
+ * 二、方法 / NVFP4 量化格式.  The GEMM epilogue records each output tile's
+ * largest |H|, so H (kept in the workspace) is read once by the encoder
+ * instead of twice.
+ *   x, Wq, Ws, Wg, bias, M, N, K, flags   as for nvfp4_linear (C is internal)
+ *   Hq  out: uint8 [M, N/2];  Hs  out: uint8 [M, N/16];  Hg  out: float [1]
+ *   ws  scratch of at least nvfp4_linear_q_workspace(M, N, K) bytes; the
+ *       bf16 H sits inside it and is overwritten by the next call.
+ * Requires N % 32 == 0 besides nvfp4_linear's conditions.
+ */
+int nvfp4_linear_q(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const float *Wg,
+                   const uint16_t *bias, int64_t M, int64_t N, int64_t K, uint32_t flags,
+                   uint8_t *Hq, uint8_t *Hs, float *Hg, void *ws, size_t ws_bytes, void *stream);
+
 /*
  * Workgroup tile (rows of A x rows of W) nvfp4_gemm uses for an M x N x K
  * problem; informational (for reporting), enqueues nothing.

@@ -188,3 +188,15 @@ def test_quantizer_flags_rejected(L):
     assert L.nvfp4_kv_append_ex(C.byref(d), FAKE, FAKE, 1, 3072, 0x30, FAKE, 1 << 20, None) == EINVAL
     assert d.n_tokens == 0 and d.n_chunks == 0
     assert b"flags" in L.nvfp4_last_error()
+
+
+def test_linear_q_rejects(L):
+    n = C.c_size_t()
+    assert L.nvfp4_linear_q_workspace(8192, 14336, 3072, C.byref(n)) == 0
+    assert n.value >= 8192 * 14336 * 2                       # holds the bf16 output
+    assert L.nvfp4_linear_q_workspace(64, 48, 64, C.byref(n)) == EINVAL      # N % 32
+    args = (FAKE, FAKE, FAKE, FAKE, None)
+    assert L.nvfp4_linear_q(*args, 64, 48, 64, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
+    assert L.nvfp4_linear_q(*args, 64, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, 16, None) == EWS
+    assert L.nvfp4_linear_q(*args, 64, 64, 64, 0x80, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
+    assert L.nvfp4_linear_q(*args, 64, 64, 64, 0, MIS, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL

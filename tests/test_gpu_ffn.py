@@ -109,3 +109,47 @@ def test_ffn_down_full_size_sampled():
     e_ref, e_64 = _sampled(hb, w.w2, rows, cols, gelu=False)
     announce(f"  normwise err vs bf16 oracle {e_ref:.3e}, vs fp64 {e_64:.3e}")
     assert e_ref <= GEMM_TOL and e_64 <= GEMM_TOL
+
+
+@pytest.mark.parametrize("M,N,K,tile", [(300, 416, 256, None), (257, 96, 512, (256, 256)),
+                                        (129, 640, 128, (128, 128)), (600, 520 - 8, 384, (256, 192)),
+                                        (64, 2048, 1024, None)])
+def test_linear_q_equals_linear_then_quantize(M, N, K, tile):
+    # the fused path (tile maxima from the GEMM epilogue, one read of H) must
+    # give exactly the bytes of the separate linear and quantise calls
+    announce(f"linear_q M={M} N={N} K={K} tile={tile}")
+    x = bf16_to_dev(workloads.random_matrix(31, M, K, 1.0, outliers=True))
+    w = nv.quantize(bf16_to_dev(workloads.random_matrix(32, N, K, 0.02)))
+    b = bf16_to_dev(workloads.random_matrix(33, 1, N, 0.5)[0])
+    hq, hs, hg = nv.linear_q(x, *w, bias=b, gelu=True, tile=tile)
+    rq, rs, rg = nv.quantize(nv.linear(x, *w, bias=b, gelu=True, tile=tile))
+    torch.cuda.synchronize()
+    assert torch.equal(hg, rg) and torch.equal(hs, rs) and torch.equal(hq, rq)
+
+
+def test_linear_q_ffn_up_full_size():
+    w = workloads.ffn()
+    announce("linear_q ffn up 8192x14336x3072 + GELU vs linear + quantise")
+    x = bf16_to_dev(w.x)
+    wq = nv.quantize(bf16_to_dev(w.w))
+    hq, hs, hg = nv.linear_q(x, *wq, gelu=True)
+    rq, rs, rg = nv.quantize(nv.linear(x, *wq, gelu=True))
+    torch.cuda.synchronize()
+    assert torch.equal(hg, rg) and torch.equal(hs, rs) and torch.equal(hq, rq)
+
+
+def test_ffn_chain_through_linear_q():
+    M, D, HID = 256, 512, 2048
+    x = workloads.random_matrix(21, M, D, 1.0, outliers=True)
+    w_up = workloads.random_matrix(22, HID, D, 0.02)
+    w_dn = workloads.random_matrix(23, D, HID, 0.02)
+    qx, qu, qd = oracle.quantize(x), oracle.quantize(w_up), oracle.quantize(w_dn)
+    _, h_ref = oracle.gemm_ref(*qx, *qu, gelu=True)
+    y64, _ = oracle.gemm_ref(*oracle.quantize(h_ref), *qd)
+    hq, hs, hg = nv.linear_q(bf16_to_dev(x), *_upload_q(qu), gelu=True)
+    y = nv.gemm(hq, hs, hg, *_upload_q(qd))
+    torch.cuda.synchronize()
+    yb = oracle.bf16_bits_to_f32(to_bits(y)).astype(np.float64)
+    err = np.linalg.norm(yb - y64) / np.linalg.norm(y64)
+    announce(f"  chain through linear_q: {err:.3e} vs fp64 chain")
+    assert err <= CHAIN_TOL
