@@ -8,18 +8,20 @@
 // Two implementations of the same arithmetic:
 //
 //   resident (one launch, the input is read once)
-//             every lane loads whole 16-element blocks (32 bytes each) and
-//             keeps them in registers; each workgroup publishes its |x| maximum
-//             in a 64-bit (call epoch, amax) slot; workgroup 0 folds the slots
-//             and publishes A the same way; every workgroup then encodes its
-//             registers, one 8-byte code store and one scale byte per block.
-//             Used whenever the whole grid fits on the device at once; a
-//             workgroup whose wait for A expires computes A from the whole
-//             input itself, so the result does not depend on residency.
-//   two-pass  k_amax (grid-stride max of |x|, one partial per block), then
-//             k_encode (every block folds the partials; each thread encodes 32
-//             consecutive elements).  Used for tensors larger than the
-//             registers of a resident grid.
+//             at most one workgroup per CU; every lane loads whole 16-element
+//             blocks (32 bytes each) and keeps them in registers; each
+//             workgroup publishes its |x| maximum in a 64-bit (call epoch,
+//             amax) slot and then polls all slots, so every workgroup derives
+//             A itself; then it encodes its registers, one 8-byte code store
+//             and one scale byte per block.  Used whenever the tensors fit in
+//             the registers of such a grid; a workgroup whose wait for A
+//             expires computes A from the whole input itself, so the result
+//             does not depend on residency.
+//   two-pass  k_amax (grid-stride max of |x|, one partial per workgroup),
+//             then k_encode (every workgroup folds the partials and encodes);
+//             lanes take consecutive 16-element blocks, four per round.  Used
+//             for larger tensors, and by itself (with the maxima a GEMM
+//             epilogue recorded) for a linear layer's NVFP4 hand-off.
 //
 // The block amax is taken on the 15-bit magnitude pattern, which orders like
 // the value for finite bf16.  With K % 32 == 0 a 32-element unit never crosses
@@ -55,6 +57,31 @@ __device__ __forceinline__ const u32x4 *unit_src(const QuantTensor &T, int64_t u
   const uint32_t col = (uint32_t)u - row * T.units_per_row;
   return reinterpret_cast<const u32x4 *>(T.x + (int64_t)row * T.ld + 32 * (int64_t)col);
 }
+// First 16-byte half of 16-element block b of the tensor (unit order).
+__device__ __forceinline__ const u32x4 *block_src(const QuantTensor &T, int64_t b) {
+  return unit_src(T, b >> 1) + 2 * (b & 1);
+}
+
+// Block b of the tensor as 8 bf16 pairs (two 16-byte loads).
+__device__ __forceinline__ void load_block(const QuantTensor &T, int64_t b, uint32_t (&w)[8]) {
+  const u32x4 *p = block_src(T, b);
+  const u32x4 lo = p[0], hi = p[1];
+  w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
+  w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+}
+
+// Largest magnitude (bf16 pattern) of 8 bf16 pairs.
+__device__ __forceinline__ uint32_t absmax16(const uint32_t (&w)[8]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m = absmax_bf16x2(m, w[j]);
+  return (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
+}
+
+// Two-pass kernels: each thread takes kTwoPassU 16-element blocks per round,
+// consecutive lanes on consecutive blocks.
+constexpr int kTwoPassU = 4;
+
 struct QuantArgs {
   QuantTensor t[2];
   ChunkMark mark;        // chunk_start == nullptr: nothing to record
@@ -62,34 +89,30 @@ struct QuantArgs {
 
 __global__ void __launch_bounds__(kThreads) k_amax(QuantArgs args) {
   const QuantTensor &T = args.t[blockIdx.y];
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t nb = 2 * T.units;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kTwoPassU;
   uint32_t m = 0;
-  int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; u + stride < T.units; u += 2 * stride) {
-    const u32x4 *p0 = unit_src(T, u), *p1 = unit_src(T, u + stride);
-    const u32x4 a0 = p0[0], a1 = p0[1], a2 = p0[2], a3 = p0[3];
-    const u32x4 b0 = p1[0], b1 = p1[1], b2 = p1[2], b3 = p1[3];
-    m = absmax_bf16x2(m, a0.x); m = absmax_bf16x2(m, a0.y); m = absmax_bf16x2(m, a0.z); m = absmax_bf16x2(m, a0.w);
-    m = absmax_bf16x2(m, a1.x); m = absmax_bf16x2(m, a1.y); m = absmax_bf16x2(m, a1.z); m = absmax_bf16x2(m, a1.w);
-    m = absmax_bf16x2(m, a2.x); m = absmax_bf16x2(m, a2.y); m = absmax_bf16x2(m, a2.z); m = absmax_bf16x2(m, a2.w);
-    m = absmax_bf16x2(m, a3.x); m = absmax_bf16x2(m, a3.y); m = absmax_bf16x2(m, a3.z); m = absmax_bf16x2(m, a3.w);
-    m = absmax_bf16x2(m, b0.x); m = absmax_bf16x2(m, b0.y); m = absmax_bf16x2(m, b0.z); m = absmax_bf16x2(m, b0.w);
-    m = absmax_bf16x2(m, b1.x); m = absmax_bf16x2(m, b1.y); m = absmax_bf16x2(m, b1.z); m = absmax_bf16x2(m, b1.w);
-    m = absmax_bf16x2(m, b2.x); m = absmax_bf16x2(m, b2.y); m = absmax_bf16x2(m, b2.z); m = absmax_bf16x2(m, b2.w);
-    m = absmax_bf16x2(m, b3.x); m = absmax_bf16x2(m, b3.y); m = absmax_bf16x2(m, b3.z); m = absmax_bf16x2(m, b3.w);
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kTwoPassU + threadIdx.x; base < nb; base += stride) {
+    uint32_t w[kTwoPassU][8];
+#pragma unroll
+    for (int i = 0; i < kTwoPassU; ++i) {
+      const int64_t b = base + (int64_t)i * kThreads;
+      if (b < nb) {
+        load_block(T, b, w[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[i][e] = 0u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTwoPassU; ++i) {
+      const uint32_t a = absmax16(w[i]);
+      m = m > a ? m : a;
+    }
   }
-  for (; u < T.units; u += stride) {
-    const u32x4 *p0 = unit_src(T, u);
-    const u32x4 a0 = p0[0], a1 = p0[1], a2 = p0[2], a3 = p0[3];
-    m = absmax_bf16x2(m, a0.x); m = absmax_bf16x2(m, a0.y); m = absmax_bf16x2(m, a0.z); m = absmax_bf16x2(m, a0.w);
-    m = absmax_bf16x2(m, a1.x); m = absmax_bf16x2(m, a1.y); m = absmax_bf16x2(m, a1.z); m = absmax_bf16x2(m, a1.w);
-    m = absmax_bf16x2(m, a2.x); m = absmax_bf16x2(m, a2.y); m = absmax_bf16x2(m, a2.z); m = absmax_bf16x2(m, a2.w);
-    m = absmax_bf16x2(m, a3.x); m = absmax_bf16x2(m, a3.y); m = absmax_bf16x2(m, a3.z); m = absmax_bf16x2(m, a3.w);
-  }
-  uint32_t mm = (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-  mm = wave_max_u32(mm);
+  m = wave_max_u32(m);
   __shared__ uint32_t red[kThreads / 64];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mm;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
@@ -162,14 +185,6 @@ struct BlockScaler {
     return S == 0 ? 0.0f : r;
   }
 };
-
-// Largest magnitude (bf16 pattern) of 8 bf16 pairs.
-__device__ __forceinline__ uint32_t absmax16(const uint32_t (&w)[8]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) m = absmax_bf16x2(m, w[j]);
-  return (m & 0xFFFFu) > (m >> 16) ? (m & 0xFFFFu) : (m >> 16);
-}
 
 // E2M1 codes of one 16-element block (8 bf16 pairs) scaled by r: element 2j
 // in the low nibble of byte j, elements 0..7 in lo, 8..15 in hi.
@@ -269,17 +284,32 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
       if (args.mark.index == 1) args.mark.chunk_start[0] = 0;
     }
   }
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x; u < T.units; u += stride) {
-    const u32x4 *src = unit_src(T, u);
-    const u32x4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
-    uint32_t b0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t b1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
-    uint32_t c0, c1, c2, c3;
-    const uint32_t s0 = encode_any<ADAPT>(b0, absmax16(b0), b6, b4, c0, c1);
-    const uint32_t s1 = encode_any<ADAPT>(b1, absmax16(b1), b6, b4, c2, c3);
-    reinterpret_cast<u32x4 *>(T.codes)[u] = u32x4{c0, c1, c2, c3};
-    T.scales[u] = (uint16_t)(s0 | (s1 << 8));
+  const int64_t nb = 2 * T.units;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kTwoPassU;
+  u32x2 *codes = reinterpret_cast<u32x2 *>(T.codes);
+  uint8_t *scales = reinterpret_cast<uint8_t *>(T.scales);
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * kTwoPassU + threadIdx.x; base < nb; base += stride) {
+    uint32_t w[kTwoPassU][8];
+#pragma unroll
+    for (int i = 0; i < kTwoPassU; ++i) {
+      const int64_t b = base + (int64_t)i * kThreads;
+      if (b < nb) {
+        load_block(T, b, w[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[i][e] = 0u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTwoPassU; ++i) {
+      const int64_t b = base + (int64_t)i * kThreads;
+      uint32_t lo, hi;
+      const uint32_t S = encode_any<ADAPT>(w[i], absmax16(w[i]), b6, b4, lo, hi);
+      if (b < nb) {
+        codes[b] = u32x2{lo, hi};
+        scales[b] = (uint8_t)S;
+      }
+    }
   }
 }
 
@@ -289,11 +319,6 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
 // Slot words: bits 63..16 the call's epoch, bits 15..0 a bf16 magnitude.
 constexpr uint64_t kEpochMask = (uint64_t(1) << 48) - 1;
 constexpr uint64_t kWaitTicks = 100000;       // 1 ms of the 100 MHz real-time counter
-
-// First 16-byte half of 16-element block b of the tensor (unit order).
-__device__ __forceinline__ const u32x4 *block_src(const QuantTensor &T, int64_t b) {
-  return unit_src(T, b >> 1) + 2 * (b & 1);
-}
 
 __device__ __forceinline__ uint64_t load_slot(const uint64_t *slot) {
   return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -531,14 +556,16 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
 // ---------------------------------------------------------------------------
 
 static int amax_blocks(int64_t units) {
-  int64_t b = (units + kThreads * 2 - 1) / (kThreads * 2);        // >= 2 units per thread
+  const int64_t per = (int64_t)kThreads * kTwoPassU;            // blocks per workgroup round
+  int64_t b = (2 * units + per - 1) / per;
   if (b < 1) b = 1;
   if (b > kAmaxBlocks) b = kAmaxBlocks;
   return (int)b;
 }
 
 static int encode_blocks(int64_t units) {
-  int64_t b = (units + kThreads - 1) / kThreads;
+  const int64_t per = (int64_t)kThreads * kTwoPassU;
+  int64_t b = (2 * units + per - 1) / per;
   if (b > 4096) b = 4096;
   if (b < 1) b = 1;
   return (int)b;
