@@ -58,6 +58,7 @@ _SIGS = {
     "nvfp4_kv_append_ex": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _i64, C.c_uint32, _p, _sz, _p],
                            C.c_int),
     "nvfp4_kv_dequant": ([C.POINTER(KVCacheDesc), _i64, _i64, _p, _p, _p], C.c_int),
+    "nvfp4_testing_set_quantize_wait": ([C.c_uint64], C.c_uint64),
     "nvfp4_strerror": ([C.c_int], C.c_char_p),
     "nvfp4_last_error": ([], C.c_char_p),
 }

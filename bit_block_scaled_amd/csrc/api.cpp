@@ -319,6 +319,8 @@ int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1, uint16_t *
   return hip_status(nvfp4::launch_kv_dequant(a, static_cast<hipStream_t>(stream)), "kv_dequant");
 }
 
+uint64_t nvfp4_testing_set_quantize_wait(uint64_t ticks) { return nvfp4::set_resident_wait_ticks(ticks); }
+
 const char *nvfp4_strerror(int status) {
   switch (status) {
     case NVFP4_OK: return "ok";

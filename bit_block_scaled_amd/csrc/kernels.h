@@ -40,6 +40,12 @@ struct ChunkMark {
 // per-tile maxima a GEMM epilogue wrote): the same bytes as launch_quantize.
 hipError_t launch_encode_from_partials(const QuantJob &job, int64_t nparts, hipStream_t stream);
 
+// Bounded wait of the single-launch quantiser for the other workgroups'
+// maxima, in ticks of the 100 MHz real-time counter; returns the previous
+// value.  The results do not depend on it (a workgroup whose wait expires
+// computes the tensor maximum itself).
+uint64_t set_resident_wait_ticks(uint64_t ticks);
+
 // Quantises one or two tensors (njobs in {1, 2}) on `stream`: one launch when
 // the grid fits on the device at once, else two launches.
 // adaptive46 selects the adaptive {4, 6} block scales.

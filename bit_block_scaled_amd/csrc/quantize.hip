@@ -319,6 +319,7 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
 // Slot words: bits 63..16 the call's epoch, bits 15..0 a bf16 magnitude.
 constexpr uint64_t kEpochMask = (uint64_t(1) << 48) - 1;
 constexpr uint64_t kWaitTicks = 100000;       // 1 ms of the 100 MHz real-time counter
+static std::atomic<uint64_t> g_wait_ticks{kWaitTicks};
 
 __device__ __forceinline__ uint64_t load_slot(const uint64_t *slot) {
   return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -362,7 +363,7 @@ constexpr int kResThreads = 1024;            // one workgroup per CU
 // result never depends on scheduling.
 template <int NJ, int UMAX, bool ADAPT>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, uint64_t epoch,
-                                                                int u) {
+                                                                int u, uint64_t wait_ticks) {
   constexpr int NW = kResThreads / 64;
   __shared__ uint32_t red[NJ][NW];
   __shared__ uint32_t shared_A[NJ];
@@ -400,7 +401,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, 
   }
 
   // poll: thread p < nwg watches slot p of every tensor
-  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + kWaitTicks;
+  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + wait_ticks;
   uint32_t a[NJ], pending = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -533,20 +534,21 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
   while (li < 4 && (1 << li) < u) ++li;
   if (li == 4 || !lim.fits[ADAPT][njobs - 1][li]) return false;
   const uint64_t epoch = next_epoch();
+  const uint64_t wt = g_wait_ticks.load();
   const dim3 grid((unsigned)nwg), block(kResThreads);
   const int ui = (int)u;
   if (njobs == 1) {
     switch (li) {
-      case 0: hipLaunchKernelGGL((k_quant_resident<1, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
-      case 1: hipLaunchKernelGGL((k_quant_resident<1, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
-      case 2: hipLaunchKernelGGL((k_quant_resident<1, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
-      default: hipLaunchKernelGGL((k_quant_resident<1, 8, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
+      case 0: hipLaunchKernelGGL((k_quant_resident<1, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<1, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
+      case 2: hipLaunchKernelGGL((k_quant_resident<1, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
+      default: hipLaunchKernelGGL((k_quant_resident<1, 8, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
     }
   } else {
     switch (li) {
-      case 0: hipLaunchKernelGGL((k_quant_resident<2, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
-      case 1: hipLaunchKernelGGL((k_quant_resident<2, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
-      default: hipLaunchKernelGGL((k_quant_resident<2, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui); break;
+      case 0: hipLaunchKernelGGL((k_quant_resident<2, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<2, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
+      default: hipLaunchKernelGGL((k_quant_resident<2, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
     }
   }
   *err = hipGetLastError();
@@ -570,6 +572,8 @@ static int encode_blocks(int64_t units) {
   if (b < 1) b = 1;
   return (int)b;
 }
+
+uint64_t set_resident_wait_ticks(uint64_t ticks) { return g_wait_ticks.exchange(ticks); }
 
 hipError_t launch_encode_from_partials(const QuantJob &job, int64_t nparts, hipStream_t stream) {
   QuantArgs a{};

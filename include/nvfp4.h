@@ -241,6 +241,15 @@ int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, 
 int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1,
                      uint16_t *K_out, uint16_t *V_out, void *stream);
 
+/*
+ * Testing hook, process-wide: the single-launch quantiser's bounded wait for
+ * the other workgroups' maxima, in ticks of the GPU's 100 MHz real-time
+ * counter (default 100000 = 1 ms).  Returns the previous value.  0 makes every
+ * workgroup take the fallback that reads the whole tensor itself; the bytes
+ * written are the same either way.  Affects launches made after the call.
+ */
+uint64_t nvfp4_testing_set_quantize_wait(uint64_t ticks);
+
 /* Human-readable name of a status code (static storage). */
 const char *nvfp4_strerror(int status);
 

@@ -123,3 +123,27 @@ def test_strided_append_from_fused_rows():
     ko, vo = gpu.dequant(0, T)
     rk, rv = ref.dequant(0, T)
     assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
+
+
+def test_many_chunks_dequant():
+    # more appends than the dequant kernel keeps in LDS (it then searches the
+    # chunk starts in global memory)
+    H, D, n = 1, 32, 2100
+    gpu = nv.KVCache(n, H, D, max_chunks=n)
+    ref = oracle.KVCacheRef(n, H, D)
+    rng = np.random.default_rng(77)
+    kall = workloads.to_bf16_bits(rng.standard_normal((n, H, D)).astype(np.float32) *
+                                  rng.uniform(0.1, 10, size=(n, 1, 1)).astype(np.float32))
+    vall = workloads.to_bf16_bits(rng.standard_normal((n, H, D)).astype(np.float32))
+    kd, vd = bf16_to_dev(kall), bf16_to_dev(vall)
+    announce(f"kv {n} one-token appends")
+    for t in range(n):
+        gpu.append(kd[t:t + 1], vd[t:t + 1])
+        ref.append(kall[t:t + 1], vall[t:t + 1])
+    ko, vo = gpu.dequant(0, n)
+    k2, v2 = gpu.dequant(1234, 1300)
+    torch.cuda.synchronize()
+    rk, rv = ref.dequant(0, n)
+    assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
+    rk2, rv2 = ref.dequant(1234, 1300)
+    assert np.array_equal(to_bits(k2), rk2) and np.array_equal(to_bits(v2), rv2)

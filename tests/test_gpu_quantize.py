@@ -129,3 +129,31 @@ def test_deterministic():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def test_bounded_wait_fallback_gives_the_same_bytes():
+    # force every workgroup of the single-launch quantiser onto the fallback
+    # (its own read of the whole tensor) from the host; the bytes must not change
+    L = nv.lib()
+    prev = L.nvfp4_testing_set_quantize_wait(0)
+    try:
+        x = workloads.random_matrix(41, 1024, 3072, sigma=1.5, outliers=True)
+        _check(x, "random 1024x3072, wait 0")
+        codes, scales, g = nv.quantize(bf16_to_dev(x), adaptive46=True)
+        rc, rs, rg = oracle.quantize(x, adaptive46=True)
+        torch.cuda.synchronize()
+        assert to_np(g)[0] == rg and np.array_equal(to_np(scales), rs) and np.array_equal(to_np(codes), rc)
+        # two tensors in one launch (a KV append)
+        rng = np.random.default_rng(42)
+        k = workloads.to_bf16_bits(rng.standard_normal((100, 24, 128)).astype(np.float32))
+        v = workloads.to_bf16_bits(3 * rng.standard_normal((100, 24, 128)).astype(np.float32))
+        kv = nv.KVCache(100, 24, 128, max_chunks=1)
+        kv.append(bf16_to_dev(k), bf16_to_dev(v))
+        ref = oracle.KVCacheRef(100, 24, 128)
+        ref.append(k, v)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(kv.k_codes), ref.k_codes) and np.array_equal(to_np(kv.v_scales), ref.v_scales)
+        assert np.array_equal(to_np(kv.gscale)[0], np.array(ref.gscale[0], dtype=np.float32))
+    finally:
+        L.nvfp4_testing_set_quantize_wait(prev)
+    assert L.nvfp4_testing_set_quantize_wait(prev) == prev
