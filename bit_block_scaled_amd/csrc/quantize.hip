@@ -29,7 +29,6 @@
 // (a KV append can read the K and V column slices of a fused QKV output in
 // place).
 #include <atomic>
-#include <chrono>
 #include <mutex>
 
 #include "device_common.h"
@@ -362,8 +361,17 @@ constexpr int kResThreads = 1024;            // one workgroup per CU
 // workgroup reads the whole tensor itself, which yields the same A, so the
 // result never depends on scheduling.
 template <int NJ, int UMAX, bool ADAPT>
-__global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, uint64_t epoch,
+__global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
                                                                 int u, uint64_t wait_ticks) {
+  // The call's epoch: one more than the word the previous call on this
+  // workspace left at slot kResidentSlots of the first tensor (any value on
+  // first use).  Every workgroup reads it before publishing its slot and it is
+  // advanced only after all slots were seen, so all workgroups agree on it;
+  // because it lives in device memory, a replayed graph gets a new epoch per
+  // replay.
+  uint64_t *eword = reinterpret_cast<uint64_t *>(args.t[0].partials) + kResidentSlots;
+  uint64_t epoch = (load_slot(eword) + 1) & kEpochMask;
+  if (epoch == 0) epoch = 1;
   constexpr int NW = kResThreads / 64;
   __shared__ uint32_t red[NJ][NW];
   __shared__ uint32_t shared_A[NJ];
@@ -429,6 +437,8 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args, 
     if (__syncthreads_or(__builtin_amdgcn_s_memrealtime() > deadline)) break;
     __builtin_amdgcn_s_sleep(1);
   }
+  if (blockIdx.x == 0 && threadIdx.x == 0)  // every workgroup has read the old word
+    __hip_atomic_store(eword, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();                          // red[] is read below
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -509,15 +519,6 @@ static const ResidentLimits &resident_limits() {
   return table[dev];
 }
 
-// Epochs identify a call's slot words; they only need to differ between calls
-// that share a workspace and from whatever the workspace held before.
-static uint64_t next_epoch() {
-  static std::atomic<uint64_t> counter{
-      (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
-  uint64_t e = counter.fetch_add(1) & kEpochMask;
-  return e == 0 ? 1 : e;
-}
-
 // Launches the resident quantiser (at most one workgroup per CU) when the
 // tensors fit in its registers; returns false (nothing launched) otherwise.
 template <bool ADAPT>
@@ -533,22 +534,21 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
   int li = 0;
   while (li < 4 && (1 << li) < u) ++li;
   if (li == 4 || !lim.fits[ADAPT][njobs - 1][li]) return false;
-  const uint64_t epoch = next_epoch();
   const uint64_t wt = g_wait_ticks.load();
   const dim3 grid((unsigned)nwg), block(kResThreads);
   const int ui = (int)u;
   if (njobs == 1) {
     switch (li) {
-      case 0: hipLaunchKernelGGL((k_quant_resident<1, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
-      case 1: hipLaunchKernelGGL((k_quant_resident<1, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
-      case 2: hipLaunchKernelGGL((k_quant_resident<1, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
-      default: hipLaunchKernelGGL((k_quant_resident<1, 8, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
+      case 0: hipLaunchKernelGGL((k_quant_resident<1, 1, ADAPT>), grid, block, 0, stream, a, ui, wt); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<1, 2, ADAPT>), grid, block, 0, stream, a, ui, wt); break;
+      case 2: hipLaunchKernelGGL((k_quant_resident<1, 4, ADAPT>), grid, block, 0, stream, a, ui, wt); break;
+      default: hipLaunchKernelGGL((k_quant_resident<1, 8, ADAPT>), grid, block, 0, stream, a, ui, wt); break;
     }
   } else {
     switch (li) {
-      case 0: hipLaunchKernelGGL((k_quant_resident<2, 1, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
-      case 1: hipLaunchKernelGGL((k_quant_resident<2, 2, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
-      default: hipLaunchKernelGGL((k_quant_resident<2, 4, ADAPT>), grid, block, 0, stream, a, epoch, ui, wt); break;
+      case 0: hipLaunchKernelGGL((k_quant_resident<2, 1, ADAPT>), grid, block, 0, stream, a, ui, wt); break;
+      case 1: hipLaunchKernelGGL((k_quant_resident<2, 2, ADAPT>), grid, block, 0, stream, a, ui, wt); break;
+      default: hipLaunchKernelGGL((k_quant_resident<2, 4, ADAPT>), grid, block, 0, stream, a, ui, wt); break;
     }
   }
   *err = hipGetLastError();

@@ -74,6 +74,12 @@ extern "C" {
 /*
  * Workspace bytes nvfp4_quantize needs for an [M, K] input (scratch for the
  * tensor-amax reduction).  Writes *bytes; the size depends only on M and K.
+ *
+ * Workspaces of every call (quantise, linear, KV append) may hold anything on
+ * first use.  The library keeps a call counter in them from one call to the
+ * next, in device memory, so calls captured in a HIP graph stay correct on
+ * every replay.  Calls that may run at the same time need separate
+ * workspaces.
  */
 int nvfp4_quantize_workspace(int64_t M, int64_t K, size_t *bytes);
 

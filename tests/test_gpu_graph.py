@@ -1,0 +1,77 @@
+"""Calls captured in a HIP graph stay correct on every replay: the quantiser's
+call counter lives in the workspace (device memory), not in the captured
+launch arguments.  Each replay runs on a new input copied in eagerly between
+replays and is checked against the oracle (quantiser) or the eager call."""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_block_scaled_amd as nv
+import oracle
+import workloads
+from gpu_helpers import announce, bf16_to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(n, M, K):
+    return [workloads.random_matrix(60 + i, M, K, sigma=0.5 + i, outliers=(i % 2 == 0)) for i in range(n)]
+
+
+@pytest.mark.parametrize("M,K", [(1024, 3072), (24 * 100, 128)])
+def test_quantize_graph_replays(M, K):
+    announce(f"graph replay of quantize {M}x{K}")
+    xs = _inputs(4, M, K)
+    x = bf16_to_dev(xs[0])
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+    g = torch.empty((1,), dtype=torch.float32, device=x.device)
+    ws = torch.empty((nv.quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=x.device)
+    nv.quantize_into(x, codes, scales, g, ws)                 # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.quantize_into(x, codes, scales, g, ws)
+    torch.cuda.synchronize()
+    for r, xb in enumerate(xs + xs[:1]):
+        x.copy_(bf16_to_dev(xb))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        rc, rs, rg = oracle.quantize(xb)
+        assert to_np(g)[0] == rg, r
+        assert np.array_equal(to_np(scales), rs) and np.array_equal(to_np(codes), rc), r
+
+
+def test_linear_and_linear_q_graph_replays():
+    M, N, K = 512, 1024, 768
+    announce(f"graph replay of linear / linear_q {M}x{N}x{K}")
+    xs = _inputs(3, M, K)
+    wq = nv.quantize(bf16_to_dev(workloads.random_matrix(70, N, K, 0.02)))
+    x = bf16_to_dev(xs[0])
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    lws = torch.empty((nv.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=x.device)
+    hq = (torch.empty((M, N // 2), dtype=torch.uint8, device=x.device),
+          torch.empty((M, N // 16), dtype=torch.uint8, device=x.device),
+          torch.empty((1,), dtype=torch.float32, device=x.device))
+    qws = torch.empty((nv.linear_q_workspace_bytes(M, N, K),), dtype=torch.uint8, device=x.device)
+    nv.linear(x, *wq, gelu=True, out=out, ws=lws)
+    nv.linear_q(x, *wq, gelu=True, out=hq, ws=qws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        nv.linear(x, *wq, gelu=True, out=out, ws=lws)
+        nv.linear_q(x, *wq, gelu=True, out=hq, ws=qws)
+    torch.cuda.synchronize()
+    for r, xb in enumerate(xs + xs[:1]):
+        x.copy_(bf16_to_dev(xb))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = nv.linear(x, *wq, gelu=True)                     # eager, fresh workspace
+        wq_h = nv.quantize(want)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), r
+        for a, b in zip(hq, wq_h):
+            assert torch.equal(a, b), r
