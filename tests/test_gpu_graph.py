@@ -75,3 +75,40 @@ def test_linear_and_linear_q_graph_replays():
         assert torch.equal(out, want), r
         for a, b in zip(hq, wq_h):
             assert torch.equal(a, b), r
+
+
+def test_kv_append_and_dequant_graph_replays():
+    # a captured append writes the token range current at capture time on
+    # every replay; its tensor scales and codes must follow each replay's input
+    H, D, T = 24, 128, 64
+    announce("graph replay of kv append + dequant")
+    rng = np.random.default_rng(80)
+    ks = [workloads.to_bf16_bits(rng.standard_normal((T, H, D)).astype(np.float32) * (1 + 3 * i))
+          for i in range(3)]
+    vs = [workloads.to_bf16_bits(rng.standard_normal((T, H, D)).astype(np.float32) / (1 + i))
+          for i in range(3)]
+    kd, vd = bf16_to_dev(ks[0]), bf16_to_dev(vs[0])
+    kv = nv.KVCache(T, H, D, max_chunks=1)
+    ko = torch.empty((T, H, D), dtype=torch.bfloat16, device=kd.device)
+    vo = torch.empty_like(ko)
+    kv.append(kd, vd)
+    kv.dequant(0, T, ko, vo)
+    torch.cuda.synchronize()
+    kv.reset()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kv.append(kd, vd)
+        kv.dequant(0, T, ko, vo)
+    torch.cuda.synchronize()
+    for r in range(4):
+        kd.copy_(bf16_to_dev(ks[r % 3]))
+        vd.copy_(bf16_to_dev(vs[r % 3]))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.KVCacheRef(T, H, D)
+        ref.append(ks[r % 3], vs[r % 3])
+        assert np.array_equal(to_np(kv.k_codes), ref.k_codes) and np.array_equal(to_np(kv.v_scales), ref.v_scales), r
+        rk, rv = ref.dequant(0, T)
+        assert np.array_equal(to_np(ko.view(torch.int16)).view(np.uint16), rk), r
+        assert np.array_equal(to_np(vo.view(torch.int16)).view(np.uint16), rv), r
