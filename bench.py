@@ -482,6 +482,13 @@ def extended(path, nv, torch, np, workloads, dev, up):
 
     seq46(); torch.cuda.synchronize()
     tseq46 = float(np.median(_time_events(torch, seq46, 5, flush)))
+    # the same 75 appends captured once in a HIP graph (each replay writes the
+    # token ranges and chunk slots fixed at capture time)
+    seq_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(seq_graph):
+        seq()
+    seq_graph.replay(); torch.cuda.synchronize()
+    tseq_graph = float(np.median(_time_events(torch, seq_graph.replay, 5, flush)))
     seq(); torch.cuda.synchronize()
     ko = torch.empty((T, 24, 128), dtype=torch.bfloat16, device=dev)
     vo = torch.empty_like(ko)
@@ -490,7 +497,8 @@ def extended(path, nv, torch, np, workloads, dev, up):
     kvb = 2 * T * 3072 * 2.5625
     lines.append({"shape": "kv_65536", "appends": len(sizes), "append_seq_us": tseq,
                   "append_seq_gbs": kvb / tseq / 1e3, "append_us_per_chunk": tseq / len(sizes),
-                  "append_seq_adaptive46_us": tseq46,
+                  "append_seq_adaptive46_us": tseq46, "append_seq_graph_us": tseq_graph,
+                  "append_seq_graph_gbs": kvb / tseq_graph / 1e3,
                   "dequant_us": tdq, "dequant_gbs": kvb / tdq / 1e3})
     with open(path, "w") as f:
         for l in lines:
