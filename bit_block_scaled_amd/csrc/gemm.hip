@@ -24,7 +24,7 @@
 // Tiling: 4 waves as 2 x 2, one wave per SIMD; each wave owns (32·WM)
 // activation rows x (32·WN) weight rows and keeps WM·WN 32x32 fp32 accumulators
 // (AGPRs).  K advances in stages of 128 elements (64 code bytes + 8 scale
-// bytes per row) through two LDS buffers: the workgroup copies stage ks+1 from
+// bytes per row in memory) through two LDS buffers: the workgroup copies stage ks+1 from
 // registers into LDS and fetches stage ks+2 from L2 into registers while it
 // computes stage ks.  Global loads move 64 contiguous bytes of a row per 4
 // lanes (buffer loads; bytes past the tile read as 0); LDS holds codes
@@ -32,12 +32,22 @@
 // fragment reads of 32 consecutive rows are free of bank conflicts.
 // Lane (r, h) reads chunk 2s + h of row r in sub-step s: k = 64s + 32h + 8t + e
 // for dword t, element e — a fixed permutation of k applied identically to
-// both operands, which leaves the sum unchanged.  Decoding, not data movement,
-// is the scarce resource (the VALU work of the fp16 fragments competes with
-// the MFMAs for issue slots): the decode of step t+1 is issued between the
-// MFMAs of step t (explicit scheduling groups), and the first decode of the
-// next stage overlaps the last MFMAs of the current one.
+// both operands, which leaves the sum unchanged.  The block scales are stored
+// in LDS already expanded to fp16 scale pairs (once per workgroup at fill
+// time).  Decoding, not data movement, is the scarce resource (the fp16
+// fragments' VALU work overlaps the MFMAs only in part): the decode of step
+// t+1 is issued between the MFMAs of step t (explicit scheduling groups), and
+// the first decode of the next stage overlaps the last MFMAs of the current
+// one.
+//
+// Launch: one workgroup per CU loops over its tiles (persistent), fetching the
+// next tile's first stage before the current epilogue; the 256x256 tile runs
+// one tile per workgroup.  The epilogue stages each wave's rows through LDS so
+// every lane stores 16 contiguous bytes of C, and can record the largest
+// |output| of each tile (the linear layer's NVFP4 hand-off).
 #include <nvfp4.h>
+
+#include <atomic>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -475,15 +485,15 @@ void gemm_tile_for(int64_t M, int64_t N, int64_t, int *bm, int *bn) {
 }
 
 static int device_cus() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];      // 0 = not queried yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Persistent launch: one workgroup per CU (the LDS ring and the registers
