@@ -42,16 +42,21 @@ PEAK_F16_TFLOPS = 2500.0         # dense fp16/bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
 PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_qkv_4096x9216x3072_pmc_traffic.txt")
-GEMM_SRC = os.path.join(ROOT, "bit_block_scaled_amd", "csrc", "gemm.hip")
+# the GEMM kernel and its host dispatch (the traffic counters are valid for these sources only)
+GEMM_SRC = [os.path.join(ROOT, "bit_block_scaled_amd", "csrc", f) for f in ("gemm_kernel.h", "gemm.hip")]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def sha256_file(p):
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def sha256_file(paths):
+    """SHA-256 over the concatenated contents of one file or a list of files."""
+    h = hashlib.sha256()
+    for p in ([paths] if isinstance(paths, str) else paths):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def parse():

@@ -24,7 +24,9 @@ BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libnvfp4.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "kv.hip"]
+# The GEMM's tile shapes are separate units (the slowest to compile), listed first.
+SOURCES = ["gemm_tile_4x4.hip", "gemm_tile_4x3.hip", "gemm_tile_3x4.hip", "gemm_tile_4x2.hip",
+           "gemm_tile_2x4.hip", "gemm_tile_2x2.hip", "quantize.hip", "gemm.hip", "kv.hip", "api.cpp"]
 ARCH = "gfx950"
 
 
@@ -59,7 +61,8 @@ def _compile(src: str) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+    workers = max(1, min(8, len(SOURCES), os.cpu_count() or 4))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
