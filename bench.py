@@ -71,6 +71,10 @@ def parse():
                          "write JSON lines to PATH")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--gemm-clock", action="store_true",
+                    help="run only the QKV GEMM, 20 launches on the benchmark's operands, then 20 on "
+                         "constant-byte operands (for rocprofv3 --pmc GRBM_GUI_ACTIVE: the clock "
+                         "under load depends on the operand bits)")
     return ap.parse_args()
 
 
@@ -186,6 +190,24 @@ def main():
     v_out = torch.empty_like(k_out)
     Kv, Vv = C[:, HD:2 * HD], C[:, 2 * HD:3 * HD]
     torch.cuda.synchronize()
+
+    if a.gemm_clock:
+        nv.quantize_into(x, aq, asc, ag, qws)
+        res = {}
+        for kind in ("benchmark", "constant"):
+            if kind == "constant":              # fixed byte patterns, every element alike
+                aq.fill_(0x35); wq.fill_(0x53); asc.fill_(0x38); wsc.fill_(0x30)
+            for _ in range(3):
+                nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, out=C)
+            ts = Timer(torch, 21)
+            for _ in range(20):
+                ts.mark()
+                nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, out=C)
+            ts.mark()
+            torch.cuda.synchronize()
+            res[kind + "_us"] = float(np.mean([ts.ev[i].elapsed_time(ts.ev[i + 1]) * 1e3 for i in range(20)]))
+        print(json.dumps({"gemm_clock": res, "launches_per_kind": 20, "warmup_per_kind": 3}))
+        return
 
     def step(t=None):
         if t: t.mark()
