@@ -66,6 +66,41 @@ def test_every_tile(tile):
     _run(600, 520, 384, 11, bias=True, tile=tile)
 
 
+TILES = [(256, 256), (256, 192), (192, 256), (256, 128), (128, 256), (128, 128)]
+
+
+@pytest.mark.parametrize("tile", TILES)
+@pytest.mark.parametrize("K", [384, 416])
+@pytest.mark.parametrize("gelu,bias", [(False, False), (False, True), (True, False), (True, True)])
+def test_every_kernel_variant(tile, K, gelu, bias):
+    """Every compiled kernel: each tile shape, with and without a K tail (K % 128 = 32), GELU and
+    bias, on a ragged 300x290 output whose first 3 rows of X are zero (without GELU their outputs
+    are the bias alone, or +0.0, bit for bit)."""
+    M, N, seed = 300, 290, 21 + K + 2 * gelu + bias
+    announce(f"gemm variant tile={tile} K={K} gelu={gelu} bias={bias}")
+    x = workloads.random_matrix(seed, M, K, 3.0 if gelu else 1.0, outliers=True)
+    x[:3] = 0
+    w = workloads.random_matrix(seed + 1000, N, K, 0.02)
+    b = workloads.random_matrix(seed + 2000, 1, N, 0.01)[0] if bias else None
+    qa, qw = oracle.quantize(x), oracle.quantize(w)
+    c64, cref = oracle.gemm_ref(*qa, *qw, bias_bits=b, gelu=gelu)
+    out = nv.gemm(*_upload_q(qa), *_upload_q(qw), bias=None if b is None else bf16_to_dev(b),
+                  gelu=gelu, tile=tile)
+    torch.cuda.synchronize()
+    got = to_bits(out)
+    e_ref, e_64 = gemm_errors(got, c64, cref)
+    assert e_ref <= GEMM_TOL and e_64 <= GEMM_TOL, (e_ref, e_64)
+    if not gelu:
+        # the zero rows are exactly the oracle's (bias, or +0.0 bit for bit)
+        assert np.array_equal(got[:3], cref[:3])
+        # away from cancellation (outputs above 1 % of the RMS, where the FP32 accumulation
+        # error stays far below a bf16 step) the result is the oracle's bf16 or a neighbour
+        vals = oracle.bf16_bits_to_f32(cref).astype(np.float64)
+        big = np.abs(vals) >= 1e-2 * np.sqrt(np.mean(vals * vals))
+        diff = np.abs(got.astype(np.int32) - cref.astype(np.int32))[big]
+        assert diff.max() <= 1 and (diff > 0).mean() < 0.01
+
+
 def test_gelu_epilogue():
     _run(256, 384, 512, 12, gelu=True, sigma_x=3.0)
 
