@@ -84,9 +84,13 @@ __device__ __forceinline__ uint32_t scale_pair_f16(uint32_t byte) {
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ float gelu_tanh(float y) {
-  // 0.5·y·(1 + tanh(z)) = y / (1 + e^(-2z)),  z = √(2/π)·(y + 0.044715·y³)
-  const float z = 0.7978845608028654f * (y + 0.044715f * y * y * y);
-  return y / (1.0f + __expf(-2.0f * z));
+  // 0.5·y·(1 + tanh z) = y / (1 + e^(-2z)),  z = √(2/π)·(y + 0.044715·y³),
+  // with e^(-2z) = 2^(y·(c1 + c2·y²)), c1 = -2·log2(e)·√(2/π), c2 = 0.044715·c1:
+  // one exp2 and one reciprocal (each about 1 ulp), no division.  Large |y|
+  // give y (exp2 → 0) or -0 (exp2 → inf, reciprocal → 0).
+  constexpr float c1 = -2.302208198144325f, c2 = -0.1029432395800235f;
+  const float t = y * (c1 + c2 * (y * y));
+  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 constexpr int kChunks = kBK / 32;        // 16-byte code chunks per row per stage
