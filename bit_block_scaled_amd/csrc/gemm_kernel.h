@@ -44,9 +44,11 @@
 //
 // Launch: one workgroup per CU loops over its tiles (persistent), fetching the
 // next tile's first stage before the current epilogue; the 256x256 tile runs
-// one tile per workgroup.  The epilogue stages each wave's rows through LDS so
-// every lane stores 16 contiguous bytes of C, and can record the largest
-// |output| of each tile (the linear layer's NVFP4 hand-off).
+// one tile per workgroup.  In the epilogue every lane stores 16 contiguous
+// bytes of a row of C: a half-wave lane swap (v_permlane32_swap) gathers them
+// from the accumulator layout for tiles inside C, an LDS staging pass for
+// tiles at the edges.  It can record the largest |output| of each tile (the
+// linear layer's NVFP4 hand-off).
 #pragma once
 
 #include <nvfp4.h>
@@ -378,16 +380,11 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
 
   // ---- epilogue: acc[j][i][v] is C[m][n] with m = (row block i) + r,
   //      n = (column block j) + 8·(v/4) + 4·h + v%4.  Each operation rounds on
-  //      its own (no fused multiply-add), as the interface states.  Each row
-  //      block is staged through the wave's own LDS region so the stores are
+  //      its own (no fused multiply-add), as the interface states.  Stores are
   //      16 contiguous bytes per lane along the rows of C.
-  __syncthreads();                       // every wave is done with the stage buffers
   uint32_t tmax = 0;                     // largest stored |bf16| pattern (tile_amax)
   {
 #pragma clang fp contract(off)
-    constexpr int PITCH = 64 * WN + 16;  // bytes per staged row (32·WN bf16 + pad)
-    constexpr int CPR = 4 * WN;          // 16-byte chunks per staged row
-    uint8_t *wreg = smem + wave * 32 * PITCH;
     const int64_t mw = cm0 + wm * 32 * WM, nw = cn0 + wn * 32 * WN;
     const bool full = (cm0 + BM <= a.M) && (cn0 + BN <= a.N) && ((a.N & 7) == 0);
     const float gg = *reinterpret_cast<const float *>(smem + T::GG);
@@ -406,58 +403,64 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
       }
 
     const bool track = a.tile_amax != nullptr;
+    // For column block j and q pair p, lane (r, h) holds columns 8q + 4h .. +3
+    // of row r for q = 2p (X) and 2p + 1 (Y).  Swapping the upper half-wave of
+    // X with the lower half-wave of Y leaves lane (r, 0) with columns
+    // 16p .. +7 and lane (r, 1) with 16p + 8 .. +15: 16 contiguous bytes.
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
+      const int64_t m = mw + 32 * i + r;
+      uint16_t *crow = a.C + m * a.N;
 #pragma unroll
       for (int j = 0; j < WN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float o[4];
+        for (int p = 0; p < 2; ++p) {
+          uint32_t xy[2][2];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            float y = acc[j][i][4 * q + k] * gg;
-            y = y + bv[j][q][k];
-            if constexpr (GELU) y = gelu_tanh(y);
-            o[k] = y;
+          for (int e = 0; e < 2; ++e) {
+            const int q = 2 * p + e;
+            float o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              float y = acc[j][i][4 * q + k] * gg;
+              y = y + bv[j][q][k];
+              if constexpr (GELU) y = gelu_tanh(y);
+              o[k] = y;
+            }
+            xy[e][0] = pack_bf16x2(o[0], o[1]);
+            xy[e][1] = pack_bf16x2(o[2], o[3]);
           }
-          *reinterpret_cast<u32x2 *>(wreg + r * PITCH + (32 * j + 8 * q + 4 * h) * 2) =
-              u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        }
-#pragma unroll
-      for (int it = 0; it < 2 * WN; ++it) {
-        const int g = it * 64 + lane;
-        const int row = g / CPR, c = g % CPR;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(wreg + row * PITCH + 16 * c);
-        const int64_t m = mw + 32 * i + row, n = nw + 8 * c;
-        uint16_t *dst = a.C + m * a.N + n;
-        if (track) {
+          const auto s0 = __builtin_amdgcn_permlane32_swap(xy[0][0], xy[1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(xy[0][1], xy[1][1], false, false);
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          const int64_t n = nw + 32 * j + 16 * p + 8 * h;
           if (full) {
-            uint32_t p = absmax_bf16x2(absmax_bf16x2(0u, v.x), v.y);
-            p = absmax_bf16x2(absmax_bf16x2(p, v.z), v.w);
-            p = (p & 0xFFFFu) > (p >> 16) ? (p & 0xFFFFu) : (p >> 16);
-            tmax = tmax > p ? tmax : p;
+            if (track) {
+              uint32_t mx = absmax_bf16x2(absmax_bf16x2(0u, v.x), v.y);
+              mx = absmax_bf16x2(absmax_bf16x2(mx, v.z), v.w);
+              mx = (mx & 0xFFFFu) > (mx >> 16) ? (mx & 0xFFFFu) : (mx >> 16);
+              tmax = tmax > mx ? tmax : mx;
+            }
+            *reinterpret_cast<u32x4 *>(crow + n) = v;
           } else if (m < a.M) {
+            // a tile at the edge: columns past N are neither stored nor counted
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            if (track) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t mag = (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu;
-              if (n + e < a.N && mag > tmax) tmax = mag;
+              for (int e = 0; e < 8; ++e) {
+                const uint32_t mag = (w[e >> 1] >> (16 * (e & 1))) & 0x7FFFu;
+                if (n + e < a.N && mag > tmax) tmax = mag;
+              }
+            }
+            if ((a.N & 7) == 0 && n + 8 <= a.N) {
+              *reinterpret_cast<u32x4 *>(crow + n) = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (n + e < a.N) crow[n + e] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
             }
           }
         }
-        if (full) {
-          *reinterpret_cast<u32x4 *>(dst) = v;
-        } else if (m < a.M) {
-          if ((a.N & 7) == 0 && n + 8 <= a.N) {
-            *reinterpret_cast<u32x4 *>(dst) = v;
-          } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (n + e < a.N) dst[e] = (uint16_t)((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          }
-        }
-      }
     }
   }
   if (a.tile_amax != nullptr) {
@@ -474,7 +477,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
   }
   if (t_next >= ntiles) break;
   t = t_next;
-  __syncthreads();                       // the staged epilogue is read before the next fills
+  __syncthreads();                       // every wave is done with the stage buffers and the
+                                         // epilogue's LDS inputs before the next tile's fills
   }
 }
 
