@@ -132,6 +132,9 @@ int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags,
  *   bias        bf16 [N] or NULL
  *   C           out: bf16 [M, N] row-major
  *   flags       NVFP4_EPI_GELU_TANH and/or one NVFP4_TILE_* hint (or 0)
+ * GELU is the tanh form 0.5·y·(1 + tanh(√(2/π)·(y + 0.044715·y³))), evaluated
+ * in binary32 as y·rcp(1 + 2^(y·(c1 + c2·y²))), c1 = −2·log2(e)·√(2/π),
+ * c2 = 0.044715·c1 (relative error below 1e-5 before the bf16 cast).
  * Requires M, N >= 1, K >= 32, K % 32 == 0.  Every scale byte must be a
  * finite E4M3 value (not 0x7F/0xFF).
  */
