@@ -111,18 +111,21 @@ def test_ffn_down_full_size_sampled():
     assert e_ref <= GEMM_TOL and e_64 <= GEMM_TOL
 
 
-@pytest.mark.parametrize("M,N,K,tile", [(300, 416, 256, None), (257, 96, 512, (256, 256)),
-                                        (129, 640, 128, (128, 128)), (600, 520 - 8, 384, (256, 192)),
-                                        (64, 2048, 1024, None)])
-def test_linear_q_equals_linear_then_quantize(M, N, K, tile):
+@pytest.mark.parametrize("M,N,K,tile,gelu", [(300, 416, 256, None, True), (257, 96, 512, (256, 256), True),
+                                             (129, 640, 128, (128, 128), True),
+                                             (600, 520 - 8, 384, (256, 192), True),
+                                             (64, 2048, 1024, None, True),
+                                             (300, 416, 416, (192, 256), False),
+                                             (257, 96, 512, (256, 128), False)])
+def test_linear_q_equals_linear_then_quantize(M, N, K, tile, gelu):
     # the fused path (tile maxima from the GEMM epilogue, one read of H) must
     # give exactly the bytes of the separate linear and quantise calls
-    announce(f"linear_q M={M} N={N} K={K} tile={tile}")
+    announce(f"linear_q M={M} N={N} K={K} tile={tile} gelu={gelu}")
     x = bf16_to_dev(workloads.random_matrix(31, M, K, 1.0, outliers=True))
     w = nv.quantize(bf16_to_dev(workloads.random_matrix(32, N, K, 0.02)))
     b = bf16_to_dev(workloads.random_matrix(33, 1, N, 0.5)[0])
-    hq, hs, hg = nv.linear_q(x, *w, bias=b, gelu=True, tile=tile)
-    rq, rs, rg = nv.quantize(nv.linear(x, *w, bias=b, gelu=True, tile=tile))
+    hq, hs, hg = nv.linear_q(x, *w, bias=b, gelu=gelu, tile=tile)
+    rq, rs, rg = nv.quantize(nv.linear(x, *w, bias=b, gelu=gelu, tile=tile))
     torch.cuda.synchronize()
     assert torch.equal(hg, rg) and torch.equal(hs, rs) and torch.equal(hq, rq)
 
