@@ -276,11 +276,11 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
 
     # --- cold (MALL and L2 flushed) timings of the HBM-bound kernels
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(torch, dev)
     cold = {"quantize": [], "kv_append": [], "kv_dequant": []}
     for _ in range(10):
         for nm in cold:
-            flush.fill_(7)
+            flush()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             if nm == "quantize":
                 e0.record(); nv.quantize_into(x, aq, asc, ag, qws); e1.record()
@@ -381,11 +381,27 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+class CacheFlush:
+    """Evicts L2 and the MALL by reading a 1 GiB buffer (written once here).
+
+    A read leaves only clean lines behind.  Writing the buffer instead would
+    leave 1 GiB of dirty lines whose write-back then competes with the timed
+    kernel's reads (the long-context X quantiser took 113 us after a write
+    flush, 76 us after a read flush)."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(7).view(torch.int64)
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        self.buf.max()
+
+
 def _time_events(torch, fn, reps, flush=None):
     ts = []
     for _ in range(reps):
         if flush is not None:
-            flush.fill_(3)
+            flush()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         fn()
@@ -410,7 +426,7 @@ def _dequant_rel_err(torch, x, codes, scales, g):
 def extended(path, nv, torch, np, workloads, dev, up):
     """Per-kernel numbers on the other DiT shapes and the full KV sequence."""
     lines = []
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(torch, dev)
     shapes = [("qkv", workloads.qkv, False), ("ffn_up", workloads.ffn, True), ("long", workloads.long_ctx, False)]
     for name, fn, gelu in shapes:
         log(f"extended: {name}")
