@@ -27,6 +27,10 @@ Parity status per function:
                          pinned (hand-worked golden blocks with their errors,
                          lossless on the amax→4 grid, never worse than amax→6
                          in binary64, exact-rational choice, invariances)
+  nvfp4.quantize(blocks2d=True), nvfp4.tile_amax_2d
+                         pinned (hand-worked tiles, W and its transpose give the
+                         transposed dequantised values, a group of equal rows
+                         reduces to the 1-D result, tile scale >= row scale)
   nvfp4.dequantize       pinned (dequant equation on round-trip inputs)
   nvfp4.gemm_ref         pinned (Fraction brute force, unit-scale special case,
                          global-scale linearity, block-sum form)
@@ -53,6 +57,7 @@ from .nvfp4 import (
     GLOBAL_DIVISOR,
     quantize,
     block_sq_error,
+    tile_amax_2d,
     dequantize,
     gemm_ref,
     gelu_tanh,
@@ -73,6 +78,7 @@ __all__ = [
     "GLOBAL_DIVISOR",
     "quantize",
     "block_sq_error",
+    "tile_amax_2d",
     "dequantize",
     "gemm_ref",
     "gelu_tanh",

@@ -36,6 +36,12 @@ Where the pages leave a step open, the readings taken are:
   R24 that error is computed in binary32, element by element in index order:
       deq = fl(fl(E2M1·S)·g) with the code's sign, e = fl(x − deq),
       err = fl(err + fl(e·e)) from err = 0.            [parity unpinned]
+  R25 two-dimensional weight blocks (二、方法 / NVFP4 训练的工程细节: weights
+      scaled in blocks along two dimensions, so W and its transpose share one
+      quantisation): a block is 16 consecutive rows (groups from row 0; the
+      last group may be shorter) by 16 consecutive elements along K; its
+      amax is the largest |x| of the tile, and every row of the tile stores
+      the tile's scale byte, so the [M, K/16] scale layout is unchanged.
 """
 
 from __future__ import annotations
@@ -61,11 +67,13 @@ E4M3_MAX = 448.0                # largest finite E4M3 value
 GLOBAL_DIVISOR = np.float32(E2M1_MAX * E4M3_MAX)   # 2688, exact in binary32
 
 
-def _encode_blocks(blocks, g, target):
+def _encode_blocks(blocks, g, target, a_blk=None):
     """Scale bytes and E2M1 magnitude codes of blocks [M, nb, 16] (|x|, binary32)
-    with each block's amax mapped to ``target`` (6 or 4): the steps R4-R7, R10."""
+    with each block's amax mapped to ``target`` (6 or 4): the steps R4-R7, R10.
+    ``a_blk`` [M, nb] overrides the per-block amax (two-dimensional blocks)."""
     div = np.float32(np.float32(target) * g)                 # fl(target·g)
-    a_blk = blocks.max(axis=2)                               # exact
+    if a_blk is None:
+        a_blk = blocks.max(axis=2)                           # exact
     s_raw = (a_blk / div).astype(np.float32)                 # fl(a / (target·g))
     S = e4m3_encode_rne_satfinite(s_raw.astype(np.float64))  # RNE, satfinite
     S_val = e4m3_decode(S).astype(np.float32)                # exact in f32
@@ -93,7 +101,19 @@ def block_sq_error(x, S, m, neg, g):
     return err
 
 
-def quantize(x_bits: np.ndarray, amax=None, adaptive46=False):
+def tile_amax_2d(ax: np.ndarray) -> np.ndarray:
+    """R25: for |x| [M, K] (binary32), the amax of each 16x16 tile, repeated on
+    every row of the tile: [M, K/16]."""
+    M, K = ax.shape
+    a1 = ax.reshape(M, K // BLOCK, BLOCK).max(axis=2)        # per row and column block
+    groups = (M + BLOCK - 1) // BLOCK
+    padded = np.zeros((groups * BLOCK, K // BLOCK), dtype=ax.dtype)
+    padded[:M] = a1                                          # |x| >= 0: padding never wins
+    a2 = padded.reshape(groups, BLOCK, K // BLOCK).max(axis=1)
+    return np.repeat(a2, BLOCK, axis=0)[:M]
+
+
+def quantize(x_bits: np.ndarray, amax=None, adaptive46=False, blocks2d=False):
     """NVFP4-quantise a bf16 matrix ``x`` [M, K] (given as uint16 bit patterns).
 
     Returns ``(codes u8 [M, K/2], scales u8 [M, K/16], g float32)``.
@@ -101,7 +121,8 @@ def quantize(x_bits: np.ndarray, amax=None, adaptive46=False):
     Rows are independent once the tensor amax A is known, so a caller may pass
     a subset of a tensor's rows together with ``amax`` = that tensor's A.
     ``adaptive46`` selects, per block, the better of the amax→6 and amax→4
-    encodings (R23, R24); the output format is unchanged.
+    encodings (R23, R24); ``blocks2d`` scales 16x16 tiles (R25); the output
+    format is unchanged either way (the two options exclude each other).
 
     The steps, in binary32 (each line one IEEE operation, nearest-even):
       A = max |x|                              (exact)
@@ -114,6 +135,10 @@ def quantize(x_bits: np.ndarray, amax=None, adaptive46=False):
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     if x_bits.ndim != 2:
         raise ValueError("x must be 2-D [M, K]")
+    if adaptive46 and blocks2d:
+        raise ValueError("adaptive46 and blocks2d exclude each other")
+    if blocks2d and amax is not None:
+        raise ValueError("blocks2d needs the whole tensor (tiles span rows)")
     M, K = x_bits.shape
     if K % BLOCK or K % 2:
         raise ValueError("K must be a multiple of 16")
@@ -139,7 +164,7 @@ def quantize(x_bits: np.ndarray, amax=None, adaptive46=False):
     g = np.float32(A / GLOBAL_DIVISOR)                       # fl(A / 2688)
 
     blocks = ax.reshape(M, K // BLOCK, BLOCK)
-    S, m = _encode_blocks(blocks, g, E2M1_MAX)
+    S, m = _encode_blocks(blocks, g, E2M1_MAX, tile_amax_2d(ax) if blocks2d else None)
     if adaptive46:
         S4, m4 = _encode_blocks(blocks, g, 4.0)
         xb = x.reshape(M, K // BLOCK, BLOCK)
