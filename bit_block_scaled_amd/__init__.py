@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     NVFP4_EPI_GELU_TANH,
     NVFP4_Q_ADAPTIVE_4_6,
+    NVFP4_Q_BLOCK_2D,
     NVFP4_TILES,
     KVCacheDesc,
     NVFP4Error,
@@ -65,23 +66,25 @@ def linear_workspace_bytes(M: int, K: int) -> int:
     return n.value
 
 
-def quantize_into(x, codes, scales, gscale, ws, adaptive46=False):
+def quantize_into(x, codes, scales, gscale, ws, adaptive46=False, blocks2d=False):
     """nvfp4_quantize (nvfp4_quantize_ex with NVFP4_Q_ADAPTIVE_4_6 when
-    ``adaptive46``) into caller-provided tensors (no allocation)."""
+    ``adaptive46``, NVFP4_Q_BLOCK_2D when ``blocks2d``) into caller-provided
+    tensors (no allocation)."""
     M, K = x.shape
     _need(x, torch.bfloat16, "x")
     _need(codes, torch.uint8, "codes", (M, K // 2))
     _need(scales, torch.uint8, "scales", (M, K // 16))
     _need(gscale, torch.float32, "gscale", (1,))
     _need(ws, torch.uint8, "ws")
-    qflags = NVFP4_Q_ADAPTIVE_4_6 if adaptive46 else 0
+    qflags = (NVFP4_Q_ADAPTIVE_4_6 if adaptive46 else 0) | (NVFP4_Q_BLOCK_2D if blocks2d else 0)
     check(lib().nvfp4_quantize_ex(_ptr(x), M, K, qflags, _ptr(codes), _ptr(scales), _ptr(gscale),
                                   _ptr(ws), ws.numel(), _stream(x.device)))
 
 
-def quantize(x: torch.Tensor, adaptive46=False):
+def quantize(x: torch.Tensor, adaptive46=False, blocks2d=False):
     """bf16 [M, K] → (codes u8 [M, K/2], scales u8 [M, K/16], gscale f32 [1]);
-    ``adaptive46`` selects the adaptive {4, 6} block scales."""
+    ``adaptive46`` selects the adaptive {4, 6} block scales, ``blocks2d`` the
+    16x16 two-dimensional blocks (for weights)."""
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, K]")
     M, K = x.shape
@@ -90,7 +93,7 @@ def quantize(x: torch.Tensor, adaptive46=False):
     scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     gscale = torch.empty((1,), dtype=torch.float32, device=dev)
     ws = torch.empty((quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
-    quantize_into(x, codes, scales, gscale, ws, adaptive46)
+    quantize_into(x, codes, scales, gscale, ws, adaptive46, blocks2d)
     return codes, scales, gscale
 
 

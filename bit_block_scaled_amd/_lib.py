@@ -22,6 +22,7 @@ NVFP4_ECAPACITY = 3
 NVFP4_EHIP = 4
 NVFP4_EPI_GELU_TANH = 0x1
 NVFP4_Q_ADAPTIVE_4_6 = 0x10
+NVFP4_Q_BLOCK_2D = 0x20
 NVFP4_TILES = {(256, 256): 0x100, (256, 192): 0x200, (192, 256): 0x300, (256, 128): 0x400,
                (128, 256): 0x500, (128, 128): 0x600}
 

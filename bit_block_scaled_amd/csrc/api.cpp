@@ -103,7 +103,9 @@ int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags, 
                       uint8_t *scales, float *gscale, void *ws, size_t ws_bytes, void *stream) {
   int s;
   if ((s = check_mk(M, K, "quantize"))) return s;
-  if (qflags & ~NVFP4_Q_ADAPTIVE_4_6) return fail(NVFP4_EINVAL, "quantize: unknown flags");
+  if (qflags & ~(NVFP4_Q_ADAPTIVE_4_6 | NVFP4_Q_BLOCK_2D)) return fail(NVFP4_EINVAL, "quantize: unknown flags");
+  if ((qflags & NVFP4_Q_ADAPTIVE_4_6) && (qflags & NVFP4_Q_BLOCK_2D))
+    return fail(NVFP4_EINVAL, "quantize: NVFP4_Q_ADAPTIVE_4_6 and NVFP4_Q_BLOCK_2D exclude each other");
   if ((s = check_ptr(x, "x"))) return s;
   if ((s = check_ptr(codes, "codes"))) return s;
   if ((s = check_ptr(scales, "scales"))) return s;
@@ -112,7 +114,8 @@ int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags, 
   if ((s = check_ptr(ws, "ws"))) return s;
   nvfp4::QuantJob j{x, codes, scales, gscale, static_cast<uint32_t *>(ws), M, K, K};
   return hip_status(nvfp4::launch_quantize(&j, 1, static_cast<hipStream_t>(stream), nullptr,
-                                           (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0),
+                                           (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0,
+                                           (qflags & NVFP4_Q_BLOCK_2D) != 0),
                     "quantize");
 }
 

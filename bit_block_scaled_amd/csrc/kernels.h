@@ -48,9 +48,12 @@ uint64_t set_resident_wait_ticks(uint64_t ticks);
 
 // Quantises one or two tensors (njobs in {1, 2}) on `stream`: one launch when
 // the grid fits on the device at once, else two launches.
-// adaptive46 selects the adaptive {4, 6} block scales.
+// adaptive46 selects the adaptive {4, 6} block scales; blocks2d the 16x16
+// two-dimensional blocks (one tensor, no mark, not with adaptive46: two
+// launches).
 hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
-                           const ChunkMark *mark = nullptr, bool adaptive46 = false);
+                           const ChunkMark *mark = nullptr, bool adaptive46 = false,
+                           bool blocks2d = false);
 
 struct GemmArgs {
   const uint8_t *Aq;

@@ -312,6 +312,45 @@ __global__ void __launch_bounds__(kThreads) k_encode(QuantArgs args, int nparts)
   }
 }
 
+// Two-dimensional blocks: 16 rows x 16 elements along K share one scale byte,
+// stored on each of the 16 rows (the [rows, K/16] scale layout is unchanged,
+// so the GEMM reads such weights as it reads any).  One thread per tile,
+// consecutive threads on consecutive column blocks of a row group, so every
+// load of a wave covers consecutive memory.  Pass 1 takes the tile's amax;
+// pass 2 reads the 16 row blocks again (from L1/L2) and encodes them with the
+// tile's scale.  Source: 二、方法 / NVFP4 训练的工程细节 (weight blocks along two
+// dimensions, so W and its transpose share one quantisation).
+__global__ void __launch_bounds__(kThreads) k_encode_2d(QuantArgs args, int nparts, int64_t rows) {
+  const QuantTensor &T = args.t[0];
+  const float g = block_global_scale(T, nparts);   // has a barrier: before any return
+  const BlockScaler b6(g, kE2M1Max);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *T.gscale = g;
+  const int64_t nbc = 2 * (int64_t)T.units_per_row;                 // 16-blocks per row
+  const int64_t tile = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (tile >= (rows + 15) / 16 * nbc) return;
+  const int64_t grp = tile / nbc, bc = tile - grp * nbc;
+  const int64_t r0 = 16 * grp, r1 = (r0 + 16 < rows) ? r0 + 16 : rows;
+  uint32_t am = 0;
+  for (int64_t r = r0; r < r1; ++r) {
+    uint32_t w[8];
+    load_block(T, r * nbc + bc, w);
+    const uint32_t a = absmax16(w);
+    am = am > a ? am : a;
+  }
+  const uint32_t S = b6.scale_byte(am);
+  const float rc = b6.recip(S);
+  u32x2 *codes = reinterpret_cast<u32x2 *>(T.codes);
+  uint8_t *scales = reinterpret_cast<uint8_t *>(T.scales);
+  for (int64_t r = r0; r < r1; ++r) {
+    uint32_t w[8], lo, hi;
+    const int64_t b = r * nbc + bc;
+    load_block(T, b, w);
+    encode_codes(w, rc, lo, hi);
+    codes[b] = u32x2{lo, hi};
+    scales[b] = (uint8_t)S;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Resident single-pass quantiser.
 
@@ -592,7 +631,7 @@ hipError_t launch_encode_from_partials(const QuantJob &job, int64_t nparts, hipS
 }
 
 hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
-                           const ChunkMark *mark, bool adaptive46) {
+                           const ChunkMark *mark, bool adaptive46, bool blocks2d) {
   QuantArgs a{};
   if (mark) a.mark = *mark;
   int64_t max_units = 0;
@@ -608,6 +647,18 @@ hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
     if (a.t[i].units > max_units) max_units = a.t[i].units;
   }
   hipError_t e = hipSuccess;
+  if (blocks2d) {             // two passes: tensor amax, then one thread per 16x16 tile
+    if (njobs != 1 || adaptive46 || mark != nullptr) return hipErrorInvalidValue;
+    const int nparts = amax_blocks(a.t[0].units);
+    hipLaunchKernelGGL(k_amax, dim3(nparts, 1), dim3(kThreads), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t tiles = (jobs[0].rows + 15) / 16 * (jobs[0].cols / 16);
+    const int64_t blocks = (tiles + kThreads - 1) / kThreads;
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_encode_2d, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a, nparts,
+                       jobs[0].rows);
+    return hipGetLastError();
+  }
   if (adaptive46 ? launch_resident<true>(a, njobs, max_units, stream, &e)
                  : launch_resident<false>(a, njobs, max_units, stream, &e))
     return e;

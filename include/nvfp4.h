@@ -67,6 +67,9 @@ extern "C" {
  * to 6 and to 4 and the encoding with the smaller binary32 squared error is
  * kept (ties to 6).  The output format is unchanged. */
 #define NVFP4_Q_ADAPTIVE_4_6 0x10u
+/* Two-dimensional 16x16 blocks for weights (nvfp4_quantize_ex only): one
+ * scale per tile of 16 rows x 16 elements, stored on each of its rows. */
+#define NVFP4_Q_BLOCK_2D 0x20u
 
 /* Alignment every device pointer must satisfy (bytes). */
 #define NVFP4_ALIGN 16
@@ -105,7 +108,8 @@ int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K,
                    void *ws, size_t ws_bytes, void *stream);
 
 /*
- * nvfp4_quantize with quantiser flags (0 or NVFP4_Q_ADAPTIVE_4_6).
+ * nvfp4_quantize with quantiser flags (0, NVFP4_Q_ADAPTIVE_4_6 or
+ * NVFP4_Q_BLOCK_2D; the two flags exclude each other).
  * Source of the adaptive mode: 二、方法 / 推理底座 (adaptive scale selection for
  * the KV chunks) and the distillation paragraph of 二、方法 (amax targets
  * {4, 6}).  With the flag, each 16-block is encoded twice: as above, and with
@@ -113,7 +117,14 @@ int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K,
  * r4 = 1/(S4·g)).  For each encoding err = Σ_i fl(e_i·e_i) accumulated in
  * binary32 in element order, e_i = fl(x_i − fl(fl(E2M1_i·S)·g)) with the
  * code's sign; the amax→4 encoding is kept only when its err is smaller.
- * Returns NVFP4_EINVAL for unknown flags; other arguments as nvfp4_quantize.
+ * NVFP4_Q_BLOCK_2D, for weights (二、方法 / NVFP4 训练的工程细节: blocks along
+ * two dimensions, so W and its transpose share one quantisation): a block is
+ * 16 consecutive rows (groups from row 0; the last may be shorter) by 16
+ * elements along K; a = the tile's max |x|, S and r as above, and the scale
+ * byte is stored on every row of the tile, so the scales keep the
+ * [M, K/16] layout and nvfp4_gemm takes such weights unchanged.  Two launches.
+ * Returns NVFP4_EINVAL for unknown or combined flags; other arguments as
+ * nvfp4_quantize.
  */
 int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags,
                       uint8_t *codes, uint8_t *scales, float *gscale,

@@ -181,13 +181,19 @@ def test_binding_refuses_cpu_tensors():
 
 def test_quantizer_flags_rejected(L):
     # unknown quantiser flags are argument errors, found before any launch
-    assert L.nvfp4_quantize_ex(FAKE, 64, 64, 0x20, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    assert L.nvfp4_quantize_ex(FAKE, 64, 64, 0x40, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
     assert L.nvfp4_quantize_ex(FAKE, 64, 64, 0x1, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    # the adaptive {4, 6} scales and the 2-D blocks exclude each other
+    both = _lib.NVFP4_Q_ADAPTIVE_4_6 | _lib.NVFP4_Q_BLOCK_2D
+    assert L.nvfp4_quantize_ex(FAKE, 64, 64, both, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    assert b"exclude" in L.nvfp4_last_error()
     d = _lib.KVCacheDesc(100, 24, 128, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0)
     assert L.nvfp4_kv_init(C.byref(d)) == 0
-    assert L.nvfp4_kv_append_ex(C.byref(d), FAKE, FAKE, 1, 3072, 0x30, FAKE, 1 << 20, None) == EINVAL
-    assert d.n_tokens == 0 and d.n_chunks == 0
-    assert b"flags" in L.nvfp4_last_error()
+    # 2-D blocks are for weights; the KV cache keeps 1-D blocks along head_dim
+    for f in (0x30, _lib.NVFP4_Q_BLOCK_2D):
+        assert L.nvfp4_kv_append_ex(C.byref(d), FAKE, FAKE, 1, 3072, f, FAKE, 1 << 20, None) == EINVAL
+        assert d.n_tokens == 0 and d.n_chunks == 0
+        assert b"flags" in L.nvfp4_last_error()
 
 
 def test_linear_q_rejects(L):
