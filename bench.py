@@ -464,6 +464,21 @@ def extended(path, nv, torch, np, workloads, dev, up):
                     rec[f"{mode}_gbs_cold"] = rows * K * 2.5625 / tt / 1e3
                     rec[f"{mode}_rel_err"] = _dequant_rel_err(torch, t, oc, os_, og)
                 lines.append(rec)
+            # two-dimensional 16x16 weight blocks (offline weight quantisation):
+            # time (cold) and normwise dequant error against the 1-D blocks
+            ws_w = torch.empty((nv.quantize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+            oc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+            os_ = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+            og = torch.empty((1,), dtype=torch.float32, device=dev)
+            rec = {"shape": "qkv_W_blocks2d", "rows": N, "K": K}
+            for mode, b2 in (("1d", False), ("2d", True)):
+                f = lambda: nv.quantize_into(W, oc, os_, og, ws_w, blocks2d=b2)
+                tt = float(np.median(_time_events(torch, f, 10, flush)))
+                f(); torch.cuda.synchronize()
+                rec[f"{mode}_us_cold"] = tt
+                rec[f"{mode}_gbs_cold"] = N * K * 2.5625 / tt / 1e3
+                rec[f"{mode}_rel_err"] = _dequant_rel_err(torch, W, oc, os_, og)
+            lines.append(rec)
         if name == "ffn_up":
             # down projection: H = GELU output (bf16 [8192, 14336]) quantised, times W_down
             Wd = up(w.w2)
