@@ -45,9 +45,9 @@
 // Launch: one workgroup per CU loops over its tiles (persistent), fetching the
 // next tile's first stage before the current epilogue; the 256x256 tile runs
 // one tile per workgroup.  In the epilogue every lane stores 16 contiguous
-// bytes of a row of C: a half-wave lane swap (v_permlane32_swap) gathers them
-// from the accumulator layout for tiles inside C, an LDS staging pass for
-// tiles at the edges.  It can record the largest |output| of each tile (the
+// bytes of a row of C, gathered from the accumulator layout by a half-wave
+// lane swap (v_permlane32_swap), with no LDS staging; tiles at the edges guard
+// their stores per lane.  It can record the largest |output| of each tile (the
 // linear layer's NVFP4 hand-off).
 #pragma once
 
