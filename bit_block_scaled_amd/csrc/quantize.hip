@@ -413,7 +413,6 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
   if (epoch == 0) epoch = 1;
   constexpr int NW = kResThreads / 64;
   __shared__ uint32_t red[NJ][NW];
-  __shared__ uint32_t shared_A[NJ];
   const int k = blockIdx.x, nwg = gridDim.x;
 
   uint32_t w[NJ][UMAX][8], bm[NJ][UMAX];
@@ -478,19 +477,33 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
   }
   if (blockIdx.x == 0 && threadIdx.x == 0)  // every workgroup has read the old word
     __hip_atomic_store(eword, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();                          // red[] is read below
+  // Every thread left the poll loop through a barrier, after its last read of
+  // red[] in the publish step, so red[] can be written again without one; the
+  // NJ tensors' maxima are folded behind a single barrier.  `done` is uniform.
+  uint32_t A[NJ];
+  if (done) {
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const uint32_t A = done ? block_max_u32<kResThreads>(a[j], red[j])
-                            : tensor_max_direct<kResThreads>(args.t[j], red[j]);
-    if (threadIdx.x == 0) shared_A[j] = A;
+    for (int j = 0; j < NJ; ++j) {
+      const uint32_t m = wave_max_u32(a[j]);
+      if ((threadIdx.x & 63) == 0) red[j][threadIdx.x >> 6] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      uint32_t r = red[j][0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) r = r > red[j][w] ? r : red[j][w];
+      A[j] = r;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) A[j] = tensor_max_direct<kResThreads>(args.t[j], red[j]);
   }
-  __syncthreads();
 
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const QuantTensor &T = args.t[j];
-    const uint32_t Abits = shared_A[j];
+    const uint32_t Abits = A[j];
     const float g = (Abits == 0) ? 1.0f : bf16_bits_to_f32(Abits) / kGlobalDivisor;
     const BlockScaler b6(g, kE2M1Max), b4(g, 4.0f);
     if (k == 0 && threadIdx.x == 0) {
