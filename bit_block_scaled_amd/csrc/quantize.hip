@@ -399,7 +399,15 @@ constexpr int kResThreads = 1024;            // one workgroup per CU
 // is bounded: if it expires (the grid was not resident all at once), the
 // workgroup reads the whole tensor itself, which yields the same A, so the
 // result never depends on scheduling.
-template <int NJ, int UMAX, bool ADAPT>
+// STREAM (one tensor, UMAX = 8): the tensor is larger than the registers of
+// the grid hold.  Its first nwg·1024·u blocks stay resident as above; the rest
+// is dealt to the workgroups in chunks of 1024 consecutive blocks, read once
+// for the maximum and once more to encode (from the MALL when it fits there).
+// Only that remainder is read twice, where the two-pass kernels read the whole
+// tensor twice.
+constexpr int kStreamU = 2;                   // streamed blocks per thread per round
+
+template <int NJ, int UMAX, bool ADAPT, bool STREAM = false>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
                                                                 int u, uint64_t wait_ticks) {
   // The call's epoch: one more than the word the previous call on this
@@ -432,9 +440,34 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
       w[j][i][4] = hi.x; w[j][i][5] = hi.y; w[j][i][6] = hi.z; w[j][i][7] = hi.w;
     }
   }
+  // streamed blocks (STREAM): b = nwg·u·1024 + (s·nwg + k)·1024 + thread
+  uint32_t ms = 0;
+  if constexpr (STREAM) {
+    const QuantTensor &T = args.t[0];
+    const int64_t nb = 2 * T.units, cstride = (int64_t)nwg * kResThreads;
+    const int64_t chunk0 = cstride * u + (int64_t)k * kResThreads + threadIdx.x;
+    for (int64_t b0 = chunk0; b0 < nb; b0 += kStreamU * cstride) {
+      uint32_t v[kStreamU][8];
+#pragma unroll
+      for (int i = 0; i < kStreamU; ++i) {
+        const int64_t b = b0 + i * cstride;
+        if (b < nb) {
+          load_block(T, b, v[i]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[i][e] = 0u;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kStreamU; ++i) {
+        const uint32_t am = absmax16(v[i]);
+        ms = ms > am ? ms : am;
+      }
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    uint32_t m = 0;
+    uint32_t m = STREAM ? ms : 0u;
 #pragma unroll
     for (int i = 0; i < UMAX; ++i) {
       bm[j][i] = absmax16(w[j][i]);
@@ -525,6 +558,33 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
         scales[b] = (uint8_t)S;
       }
     }
+    if constexpr (STREAM) {
+      const int64_t nb = 2 * T.units, cstride = (int64_t)nwg * kResThreads;
+      const int64_t chunk0 = cstride * u + (int64_t)k * kResThreads + threadIdx.x;
+      for (int64_t b0 = chunk0; b0 < nb; b0 += kStreamU * cstride) {
+        uint32_t v[kStreamU][8];
+#pragma unroll
+        for (int i = 0; i < kStreamU; ++i) {
+          const int64_t b = b0 + i * cstride;
+          if (b < nb) {
+            load_block(T, b, v[i]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i][e] = 0u;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < kStreamU; ++i) {
+          const int64_t b = b0 + i * cstride;
+          uint32_t lo, hi;
+          const uint32_t S = encode_any<ADAPT>(v[i], absmax16(v[i]), b6, b4, lo, hi);
+          if (b < nb) {
+            codes[b] = u32x2{lo, hi};
+            scales[b] = (uint8_t)S;
+          }
+        }
+      }
+    }
   }
 }
 
@@ -533,11 +593,12 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
 struct ResidentLimits {
   int cus = 0;
   bool fits[2][2][4] = {};                // [ADAPT][NJ - 1][log2 UMAX]
+  bool fits_stream[2] = {};               // [ADAPT]: the STREAM kernel (one tensor, UMAX 8)
 };
 
-template <int NJ, int UMAX, bool ADAPT>
+template <int NJ, int UMAX, bool ADAPT, bool STREAM = false>
 static const void *resident_fn() {
-  return reinterpret_cast<const void *>(&k_quant_resident<NJ, UMAX, ADAPT>);
+  return reinterpret_cast<const void *>(&k_quant_resident<NJ, UMAX, ADAPT, STREAM>);
 }
 
 static const ResidentLimits &resident_limits() {
@@ -566,6 +627,12 @@ static const ResidentLimits &resident_limits() {
                                                                          0) == hipSuccess &&
                             n >= 1;
         }
+    const void *sfns[2] = {resident_fn<1, 8, false, true>(), resident_fn<1, 8, true, true>()};
+    for (int a = 0; a < 2; ++a) {
+      int n = 0;
+      r.fits_stream[a] = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sfns[a], kResThreads, 0) ==
+                             hipSuccess && n >= 1;
+    }
     filled[dev] = true;
   }
   return table[dev];
@@ -585,8 +652,17 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
   const int64_t u = (nb + nwg * kResThreads - 1) / (nwg * kResThreads);
   int li = 0;
   while (li < 4 && (1 << li) < u) ++li;
-  if (li == 4 || !lim.fits[ADAPT][njobs - 1][li]) return false;
   const uint64_t wt = g_wait_ticks.load();
+  if (li == 4) {
+    // more than the grid's registers hold: keep 8 blocks per thread resident
+    // and stream the rest (one tensor only; else the two-pass kernels)
+    if (njobs != 1 || !lim.fits_stream[ADAPT]) return false;
+    hipLaunchKernelGGL((k_quant_resident<1, 8, ADAPT, true>), dim3((unsigned)nwg), dim3(kResThreads), 0,
+                       stream, a, 8, wt);
+    *err = hipGetLastError();
+    return true;
+  }
+  if (!lim.fits[ADAPT][njobs - 1][li]) return false;
   const dim3 grid((unsigned)nwg), block(kResThreads);
   const int ui = (int)u;
   if (njobs == 1) {

@@ -121,6 +121,25 @@ def test_ffn_hidden_shape_sampled_rows():
     _check(hb, "H-shaped [8192,14336] sampled rows", rows=rows, amax=A)
 
 
+@pytest.mark.parametrize("M,K,seed", [(11000, 3072, 51), (81000, 416, 52)])
+def test_streamed_beyond_register_capacity(M, K, seed):
+    # just past what 256 workgroups x 1024 threads x 8 blocks hold: the first
+    # blocks stay in registers, the rest is streamed (read twice); whole-tensor
+    # bit-exactness, standard and adaptive, and with the wait forced to expire
+    x = workloads.random_matrix(seed, M, K, 1.0, outliers=True)
+    _check(x, f"streamed {M}x{K}")
+    codes, scales, g = nv.quantize(bf16_to_dev(x), adaptive46=True)
+    rc, rs, rg = oracle.quantize(x, adaptive46=True)
+    torch.cuda.synchronize()
+    assert to_np(g)[0] == rg and np.array_equal(to_np(scales), rs) and np.array_equal(to_np(codes), rc)
+    L = nv.lib()
+    prev = L.nvfp4_testing_set_quantize_wait(0)
+    try:
+        _check(x, f"streamed {M}x{K}, wait 0")
+    finally:
+        L.nvfp4_testing_set_quantize_wait(prev)
+
+
 def test_deterministic():
     w = workloads.qkv()
     x = bf16_to_dev(w.x)
