@@ -92,3 +92,40 @@ def test_dequant_uses_each_chunks_scale():
         assert np.linalg.norm(x - y) / np.linalg.norm(x) < 0.15
     with pytest.raises(ValueError):
         c.dequant(0, 16)
+
+
+def _hand_example_input(golden):
+    """The one-token input of the hand-worked dequant example as bf16 bits [1, 1, 32]."""
+    g = golden("kv_dequant_hand_example.txt")
+    x = np.zeros(32, np.float32)
+    x[0] = oracle.bf16_bits_to_f32(np.array([int(g["amax_bits"][0], 16)], np.uint16))[0]
+    m, e = (int(v) for v in g["block_amax"])
+    x[16] = np.ldexp(np.float32(m), e)
+    m, e = (int(v) for v in g["element"])
+    x[17] = np.ldexp(np.float32(m), e)
+    x[18] = -x[17]
+    return g, to_bf16_bits(x).reshape(1, 1, 32)
+
+
+def test_dequant_hand_example_non_power_of_two_scale(golden):
+    # g = 8738133·2^-34: the binary32 product lands on a bf16 tie, so the
+    # two-rounding chain, one rounding from binary64 and the other association
+    # of the three factors give different bytes (worked by hand in the fixture)
+    g, k = _hand_example_input(golden)
+    c = oracle.KVCacheRef(1, 1, 32)
+    c.append(k, k)
+    gk = np.float32(c.gscale[0][0])
+    assert gk.view(np.uint32) == int(g["g_bits"][0], 16)
+    assert c.k_scales[0, 0, 1] == int(g["scale_byte"][0], 16)
+    codes = oracle.unpack_nibbles(c.k_codes[0, 0])
+    assert codes[17] == int(g["code"][0], 16) and codes[18] == int(g["code"][0], 16) | 8
+    ko, _ = c.dequant(0, 1)
+    assert ko[0, 0, 17] == int(g["expected"][0], 16)
+    assert ko[0, 0, 18] == int(g["expected_negative"][0], 16)
+    # the readings a mistake could take differ here, so the pin separates them
+    exact = oracle.dequantize(c.k_codes[0], c.k_scales[0], gk)[0, 17]          # binary64, exact
+    assert oracle.bf16_rne_from_f64(exact) == int(g["one_rounding"][0], 16)
+    s = np.float32(oracle.e4m3_decode(c.k_scales[0, 0, 1]))
+    alt = np.float32(np.float32(1.5) * np.float32(s * gk))
+    assert oracle.bf16_rne_from_f64(np.float64(alt)) == int(g["other_association"][0], 16)
+    assert int(g["expected"][0], 16) != int(g["one_rounding"][0], 16)
