@@ -183,7 +183,7 @@ def main():
     aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     asc = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     ag = torch.empty((1,), dtype=torch.float32, device=dev)
-    qws = torch.empty((nv.quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+    qws = nv.workspace(nv.quantize_workspace_bytes(M, K), dev)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     kv = nv.KVCache(M, 24, 128, max_chunks=1, device=dev)
     k_out = torch.empty((M, 24, 128), dtype=torch.bfloat16, device=dev)
@@ -440,7 +440,7 @@ def extended(path, nv, torch, np, workloads, dev, up):
         g = lambda: nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, gelu=gelu, out=C)
         g(); torch.cuda.synchronize()
         tg = float(np.median(_time_events(torch, g, 20)))
-        qws = torch.empty((nv.quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+        qws = nv.workspace(nv.quantize_workspace_bytes(M, K), dev)
         q = lambda: nv.quantize_into(x, aq, asc, ag, qws)
         tq = float(np.median(_time_events(torch, q, 20, flush)))
         qb = M * K * 2.5625
@@ -451,7 +451,7 @@ def extended(path, nv, torch, np, workloads, dev, up):
             # adaptive {4, 6} block scales: time (cold) and normwise dequant error
             # against the standard amax→6 encoding, for X and for the weights
             for tname, t, rows in (("X", x, M), ("W", W, N)):
-                ws_t = torch.empty((nv.quantize_workspace_bytes(rows, K),), dtype=torch.uint8, device=dev)
+                ws_t = nv.workspace(nv.quantize_workspace_bytes(rows, K), dev)
                 oc = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
                 os_ = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
                 og = torch.empty((1,), dtype=torch.float32, device=dev)
@@ -466,7 +466,7 @@ def extended(path, nv, torch, np, workloads, dev, up):
                 lines.append(rec)
             # two-dimensional 16x16 weight blocks (offline weight quantisation):
             # time (cold) and normwise dequant error against the 1-D blocks
-            ws_w = torch.empty((nv.quantize_workspace_bytes(N, K),), dtype=torch.uint8, device=dev)
+            ws_w = nv.workspace(nv.quantize_workspace_bytes(N, K), dev)
             oc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
             os_ = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
             og = torch.empty((1,), dtype=torch.float32, device=dev)
@@ -488,7 +488,7 @@ def extended(path, nv, torch, np, workloads, dev, up):
             gd = lambda: nv.gemm(hq, hsc, hg, dq, dsc, dg, out=Cd)
             gd(); torch.cuda.synchronize()
             td = float(np.median(_time_events(torch, gd, 20)))
-            hws = torch.empty((nv.quantize_workspace_bytes(M, N),), dtype=torch.uint8, device=dev)
+            hws = nv.workspace(nv.quantize_workspace_bytes(M, N), dev)
             qh = lambda: nv.quantize_into(C, hq, hsc, hg, hws)
             tqh = float(np.median(_time_events(torch, qh, 20, flush)))
             lines.append({"shape": "ffn_down", "M": M, "N": K, "K": N, "gemm_us": td,
@@ -496,8 +496,8 @@ def extended(path, nv, torch, np, workloads, dev, up):
                           "quantize_us_cold": tqh, "quantize_gbs_cold": M * N * 2.5625 / tqh / 1e3})
             # the whole FFN: linear(up, GELU) → quantise H → down GEMM, against
             # linear_q (H's maxima from the up GEMM's epilogue, H read once)
-            lws = torch.empty((nv.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
-            qws_ = torch.empty((nv.linear_q_workspace_bytes(M, N, K),), dtype=torch.uint8, device=dev)
+            lws = nv.workspace(nv.linear_workspace_bytes(M, K), dev)
+            qws_ = nv.workspace(nv.linear_q_workspace_bytes(M, N, K), dev)
 
             def chain():
                 nv.linear(x, wq, wsc, wg, gelu=True, out=C, ws=lws)

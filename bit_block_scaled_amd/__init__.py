@@ -30,7 +30,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["quantize", "quantize_into", "gemm", "linear", "linear_q", "KVCache", "NVFP4Error", "lib",
-           "gemm_tile", "quantize_workspace_bytes", "linear_workspace_bytes", "linear_q_workspace_bytes"]
+           "gemm_tile", "workspace", "quantize_workspace_bytes", "linear_workspace_bytes",
+           "linear_q_workspace_bytes"]
 
 
 def _stream(device=None):
@@ -52,6 +53,12 @@ def _need(t, dtype, name, shape=None):
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A workspace of ``nbytes`` bytes in the state the library requires before
+    its first use: all zero.  Reuse it for later calls on the same stream."""
+    return torch.zeros((nbytes,), dtype=torch.uint8, device=device)
 
 
 def quantize_workspace_bytes(M: int, K: int) -> int:
@@ -92,7 +99,7 @@ def quantize(x: torch.Tensor, adaptive46=False, blocks2d=False):
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     gscale = torch.empty((1,), dtype=torch.float32, device=dev)
-    ws = torch.empty((quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=dev)
+    ws = workspace(quantize_workspace_bytes(M, K), dev)
     quantize_into(x, codes, scales, gscale, ws, adaptive46, blocks2d)
     return codes, scales, gscale
 
@@ -130,8 +137,9 @@ def gemm(Aq, As, Ag, Wq, Ws, Wg, bias=None, gelu=False, out=None, tile=None):
 
 def linear(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, ws=None, tile=None):
     """The W4A4 linear layer: quantise bf16 x [M, K] per call, then GEMM with
-    pre-quantised weights.  ``ws`` (uint8, ≥ linear_workspace_bytes) may be
-    passed to avoid an allocation per call."""
+    pre-quantised weights.  ``ws`` (uint8, ≥ linear_workspace_bytes, zero
+    before its first use: see :func:`workspace`) may be passed to avoid an
+    allocation per call."""
     M, K = x.shape
     N = Wq.shape[0]
     _need(x, torch.bfloat16, "x")
@@ -144,7 +152,7 @@ def linear(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, ws=None, tile=None):
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need(out, torch.bfloat16, "out", (M, N))
     if ws is None:
-        ws = torch.empty((linear_workspace_bytes(M, K),), dtype=torch.uint8, device=x.device)
+        ws = workspace(linear_workspace_bytes(M, K), x.device)
     _need(ws, torch.uint8, "ws")
     flags = _flags(gelu, tile)
     check(lib().nvfp4_linear(_ptr(x), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias), _ptr(out),
@@ -179,7 +187,7 @@ def linear_q(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, ws=None, tile=None)
     _need(Hs, torch.uint8, "Hs", (M, N // 16))
     _need(Hg, torch.float32, "Hg", (1,))
     if ws is None:
-        ws = torch.empty((linear_q_workspace_bytes(M, N, K),), dtype=torch.uint8, device=x.device)
+        ws = workspace(linear_q_workspace_bytes(M, N, K), x.device)
     _need(ws, torch.uint8, "ws")
     flags = _flags(gelu, tile)
     check(lib().nvfp4_linear_q(_ptr(x), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias), M, N, K, flags,
@@ -246,7 +254,7 @@ class KVCache:
             ld = K.stride(0)
         if ws is None:
             if self._ws is None or self._ws.numel() < self.workspace_bytes(T):
-                self._ws = torch.empty((self.workspace_bytes(T),), dtype=torch.uint8, device=self.device)
+                self._ws = workspace(self.workspace_bytes(T), self.device)
             ws = self._ws
         qflags = NVFP4_Q_ADAPTIVE_4_6 if adaptive46 else 0
         check(lib().nvfp4_kv_append_ex(C.byref(self.desc), _ptr(K), _ptr(V), T, ld, qflags, _ptr(ws),

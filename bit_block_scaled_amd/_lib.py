@@ -13,7 +13,8 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "lib", "libnvfp4.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "nvfp4.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADERS = [os.path.join(INCLUDE, h) for h in ("nvfp4.h", "nvfp4_testing.h")]
 
 NVFP4_OK = 0
 NVFP4_EINVAL = 1
@@ -73,10 +74,12 @@ class NVFP4Error(RuntimeError):
         self.status = status
 
 
-def header_symbols(path: str = HEADER):
-    """Function names declared in include/nvfp4.h."""
-    text = open(path).read()
-    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", text)))
+def header_symbols(paths=None):
+    """Function names declared in the public headers under include/."""
+    names = set()
+    for path in paths or HEADERS:
+        names |= set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", open(path).read()))
+    return sorted(names)
 
 
 def lib():

@@ -2,9 +2,11 @@
 // kernel launches.  Every entry point is declared (with its contract) in
 // include/nvfp4.h.
 #include <nvfp4.h>
+#include <nvfp4_testing.h>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <string>
 
@@ -12,10 +14,15 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// The calling thread's last error message.  A plain character array: it has
+// no destructor, so nothing of this library runs when a thread or the process
+// exits.
+thread_local char g_last_error[512];
 
 int fail(int status, const std::string &msg) {
-  g_last_error = msg;
+  const size_t n = msg.size() < sizeof(g_last_error) - 1 ? msg.size() : sizeof(g_last_error) - 1;
+  memcpy(g_last_error, msg.data(), n);
+  g_last_error[n] = '\0';
   return status;
 }
 
@@ -112,7 +119,7 @@ int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags, 
   if ((s = check_ptr(gscale, "gscale", 4))) return s;
   if (ws == nullptr || ws_bytes < kQuantWs) return fail(NVFP4_EWORKSPACE, "quantize: workspace too small");
   if ((s = check_ptr(ws, "ws"))) return s;
-  nvfp4::QuantJob j{x, codes, scales, gscale, static_cast<uint32_t *>(ws), M, K, K};
+  nvfp4::QuantJob j{x, codes, scales, gscale, ws, M, K, K};
   return hip_status(nvfp4::launch_quantize(&j, 1, static_cast<hipStream_t>(stream), nullptr,
                                            (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0,
                                            (qflags & NVFP4_Q_BLOCK_2D) != 0),
@@ -162,7 +169,7 @@ int nvfp4_linear(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const 
   uint8_t *as = base + w.scales;
   float *ag = reinterpret_cast<float *>(base + w.gscale);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  nvfp4::QuantJob j{x, aq, as, ag, reinterpret_cast<uint32_t *>(base + w.partials), M, K, K};
+  nvfp4::QuantJob j{x, aq, as, ag, base + w.partials, M, K, K};
   if ((s = hip_status(nvfp4::launch_quantize(&j, 1, st), "linear/quantize"))) return s;
   nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, C, M, N, K, flags};
   return hip_status(nvfp4::launch_gemm(a, st), "linear/gemm");
@@ -217,15 +224,15 @@ int nvfp4_linear_q(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, cons
   float *ag = reinterpret_cast<float *>(base + w.lin.gscale);
   uint32_t *slots = reinterpret_cast<uint32_t *>(base + w.slots);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  nvfp4::QuantJob jx{x, aq, as, ag, reinterpret_cast<uint32_t *>(base + w.lin.partials), M, K, K};
+  nvfp4::QuantJob jx{x, aq, as, ag, base + w.lin.partials, M, K, K};
   if ((s = hip_status(nvfp4::launch_quantize(&jx, 1, st), "linear_q/quantize"))) return s;
   nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, H, M, N, K, flags};
   a.tile_amax = slots;
   const int64_t tiles = nvfp4::gemm_tile_count(a);
   if (tiles > w.max_tiles) return fail(NVFP4_EHIP, "linear_q: internal tile count exceeds the workspace");
   if ((s = hip_status(nvfp4::launch_gemm(a, st), "linear_q/gemm"))) return s;
-  nvfp4::QuantJob jh{H, Hq, Hs, Hg, slots, M, N, N};
-  return hip_status(nvfp4::launch_encode_from_partials(jh, tiles, st), "linear_q/encode");
+  nvfp4::QuantJob jh{H, Hq, Hs, Hg, nullptr, M, N, N};
+  return hip_status(nvfp4::launch_encode_from_partials(jh, slots, tiles, st), "linear_q/encode");
 }
 
 int nvfp4_kv_init(nvfp4_kv_cache *c) {
@@ -278,11 +285,11 @@ int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, 
   if ((s = check_ptr(ws, "ws"))) return s;
   const int64_t e = c->heads * c->head_dim;           // elements per token
   const int64_t off = c->n_tokens * e;
-  uint32_t *parts = static_cast<uint32_t *>(ws);
+  uint8_t *parts = static_cast<uint8_t *>(ws);
   nvfp4::QuantJob jobs[2] = {
       {K, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T, e, ld},
       {V, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
-       parts + kQuantWs / sizeof(uint32_t), T, e, ld}};
+       parts + kQuantWs, T, e, ld}};
   nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
   s = hip_status(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark,
                                         (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0),
@@ -335,6 +342,6 @@ const char *nvfp4_strerror(int status) {
   }
 }
 
-const char *nvfp4_last_error(void) { return g_last_error.c_str(); }
+const char *nvfp4_last_error(void) { return g_last_error; }
 
 }  // extern "C"

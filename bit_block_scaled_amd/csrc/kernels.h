@@ -8,22 +8,30 @@ namespace nvfp4 {
 
 // Upper bound on the number of amax partials a two-pass quantisation writes.
 constexpr int kAmaxBlocks = 1024;
-// Slots of a resident (single-pass) quantisation: one 64-bit word per
-// workgroup plus the published result at index kResidentSlots.
-constexpr int kResidentSlots = 4096;
-// Scratch bytes per quantised tensor (covers both uses; a multiple of 256).
-constexpr size_t kQuantScratchBytes = 8 * (size_t(kResidentSlots) + 32);
+// Most workgroups of a resident (single-pass) quantisation: one 64-bit slot
+// each, every slot polled by one thread of a 1024-thread workgroup.
+constexpr int kResidentSlots = 1024;
+// Scratch of one quantised tensor, 256-byte aligned, all zero before its first
+// use (the library keeps it valid from one call to the next):
+//   [0, kCtrlOffset)                 resident slots, one (epoch, max) word per workgroup
+//   [kCtrlOffset, kPartialsOffset)   control words: [0] the epoch of the last
+//                                    completed resident call, [1] its arrival counter
+//   [kPartialsOffset, kQuantScratchBytes)  partial maxima of the two-pass kernels
+constexpr size_t kCtrlOffset = 8 * size_t(kResidentSlots);
+constexpr size_t kPartialsOffset = kCtrlOffset + 256;
+constexpr size_t kQuantScratchBytes = kPartialsOffset + 4 * size_t(kAmaxBlocks);
+static_assert(kQuantScratchBytes % 256 == 0, "scratch regions stay 256-byte aligned");
 
 // One tensor to quantise: `rows` rows of `cols` bf16 values (cols a multiple of
 // 32), row r starting at x + r·ld, into dense codes (rows·cols/2 bytes),
-// scales (rows·cols/16 bytes) and *gscale, using `partials`
-// (kQuantScratchBytes, 8-byte aligned) as scratch.  A dense matrix may be passed as one row.
+// scales (rows·cols/16 bytes) and *gscale, using `scratch`
+// (kQuantScratchBytes, laid out as above).  A dense matrix may be passed as one row.
 struct QuantJob {
   const uint16_t *x;
   uint8_t *codes;
   uint8_t *scales;
   float *gscale;
-  uint32_t *partials;
+  void *scratch;
   int64_t rows, cols, ld;
 };
 
@@ -36,9 +44,11 @@ struct ChunkMark {
 };
 
 // Encodes one tensor in a single pass when its |x| maximum is already known as
-// the largest of `nparts` 15-bit bf16 magnitude patterns at job.partials (the
+// the largest of `nparts` 15-bit bf16 magnitude patterns at `maxima` (the
 // per-tile maxima a GEMM epilogue wrote): the same bytes as launch_quantize.
-hipError_t launch_encode_from_partials(const QuantJob &job, int64_t nparts, hipStream_t stream);
+// job.scratch is not used.
+hipError_t launch_encode_from_partials(const QuantJob &job, const uint32_t *maxima, int64_t nparts,
+                                       hipStream_t stream);
 
 // Bounded wait of the single-launch quantiser for the other workgroups'
 // maxima, in ticks of the 100 MHz real-time counter; returns the previous

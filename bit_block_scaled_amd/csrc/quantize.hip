@@ -15,8 +15,8 @@
 //             A itself; then it encodes its registers, one 8-byte code store
 //             and one scale byte per block.  Used whenever the tensors fit in
 //             the registers of such a grid; a workgroup whose wait for A
-//             expires computes A from the whole input itself, so the result
-//             does not depend on residency.
+//             expires reads the shares of the workgroups it has not heard
+//             from itself, so the result does not depend on residency.
 //   two-pass  k_amax (grid-stride max of |x|, one partial per workgroup),
 //             then k_encode (every workgroup folds the partials and encodes);
 //             lanes take consecutive 16-element blocks, four per round.  Used
@@ -44,7 +44,8 @@ struct QuantTensor {
   uint8_t *codes;        // 16 bytes per 32-element unit
   uint16_t *scales;      // 2 scale bytes per unit
   float *gscale;         // where g is written
-  uint32_t *partials;    // kAmaxBlocks partial maxima
+  uint64_t *slots;       // resident launch: kResidentSlots slots, then the control words
+  uint32_t *partials;    // two-pass launch: kAmaxBlocks partial maxima
   int64_t units;         // elements / 32
   uint32_t units_per_row;
   int64_t ld;            // input elements between row starts
@@ -374,22 +375,36 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t *red) {
   return r;
 }
 
-// |x| maximum of a whole tensor read by one workgroup of NT threads (the
-// fallback when the other workgroups' maxima do not arrive in time).
-template <int NT>
-__device__ uint32_t tensor_max_direct(const QuantTensor &T, uint32_t *red) {
-  uint32_t m = 0;
-  for (int64_t b = threadIdx.x; b < 2 * T.units; b += NT) {
-    const u32x4 *p = block_src(T, b);
-    const u32x4 lo = p[0], hi = p[1];
-    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    const uint32_t a = absmax16(w);
-    m = m > a ? m : a;
-  }
-  return block_max_u32<NT>(m, red);
-}
-
 constexpr int kResThreads = 1024;            // one workgroup per CU
+constexpr int kStreamU = 2;                   // streamed blocks per thread per round
+
+// This thread's part of the |x| maximum of workgroup p's share of a tensor
+// (the blocks that workgroup p loads, including its streamed chunks): read by
+// a workgroup whose wait for p's slot expired.
+template <bool STREAM>
+__device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
+  const int64_t nb = 2 * T.units;
+  uint32_t m = 0;
+  for (int i = 0; i < u; ++i) {
+    const int64_t b = ((int64_t)p * u + i) * kResThreads + threadIdx.x;
+    if (b < nb) {
+      uint32_t w[8];
+      load_block(T, b, w);
+      const uint32_t a = absmax16(w);
+      m = m > a ? m : a;
+    }
+  }
+  if constexpr (STREAM) {
+    const int64_t cstride = (int64_t)nwg * kResThreads;
+    for (int64_t b = cstride * u + (int64_t)p * kResThreads + threadIdx.x; b < nb; b += cstride) {
+      uint32_t w[8];
+      load_block(T, b, w);
+      const uint32_t a = absmax16(w);
+      m = m > a ? m : a;
+    }
+  }
+  return m;
+}
 
 // Workgroup k owns, in each of the NJ tensors, the 16-element blocks
 // (k·u + i)·1024 + thread, i < u <= UMAX; a thread loads a block as two
@@ -397,30 +412,34 @@ constexpr int kResThreads = 1024;            // one workgroup per CU
 // maximum per tensor in slot k, then polls all slots of the grid (one load per
 // thread), so every workgroup derives A itself after one round trip.  The wait
 // is bounded: if it expires (the grid was not resident all at once), the
-// workgroup reads the whole tensor itself, which yields the same A, so the
-// result never depends on scheduling.
+// workgroup reads the shares of the workgroups whose slots it has not seen
+// itself, which yields the same A, so the result never depends on scheduling.
+//
+// The epoch that tags the slots of a call is one more than the control word
+// the previous call on the workspace left (0 in a zeroed workspace).  After
+// its poll every workgroup adds one to the arrival counter beside that word;
+// the workgroup that completes the count resets the counter and advances the
+// word.  Every workgroup reads the word before it arrives, so all workgroups of
+// a call use the same epoch even when they do not run at the same time, and a
+// slot is never tagged with an epoch later than the word: a slot left by an
+// earlier call is never taken for a current one.  Because the word lives in
+// device memory, each replay of a captured graph gets a new epoch.
 // STREAM (one tensor, UMAX = 8): the tensor is larger than the registers of
 // the grid hold.  Its first nwg·1024·u blocks stay resident as above; the rest
 // is dealt to the workgroups in chunks of 1024 consecutive blocks, read once
 // for the maximum and once more to encode (from the MALL when it fits there).
 // Only that remainder is read twice, where the two-pass kernels read the whole
 // tensor twice.
-constexpr int kStreamU = 2;                   // streamed blocks per thread per round
-
 template <int NJ, int UMAX, bool ADAPT, bool STREAM = false>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
                                                                 int u, uint64_t wait_ticks) {
-  // The call's epoch: one more than the word the previous call on this
-  // workspace left at slot kResidentSlots of the first tensor (any value on
-  // first use).  Every workgroup reads it before publishing its slot and it is
-  // advanced only after all slots were seen, so all workgroups agree on it;
-  // because it lives in device memory, a replayed graph gets a new epoch per
-  // replay.
-  uint64_t *eword = reinterpret_cast<uint64_t *>(args.t[0].partials) + kResidentSlots;
-  uint64_t epoch = (load_slot(eword) + 1) & kEpochMask;
+  // the call's epoch (control words: [0] last completed epoch, [1] arrivals)
+  uint64_t *ctrl = args.t[0].slots + kResidentSlots;
+  uint64_t epoch = (load_slot(ctrl) + 1) & kEpochMask;
   if (epoch == 0) epoch = 1;
   constexpr int NW = kResThreads / 64;
-  __shared__ uint32_t red[NJ][NW];
+  __shared__ uint32_t red[NJ][NW], red2[NJ][NW];
+  __shared__ uint64_t miss[NJ][NW];
   const int k = blockIdx.x, nwg = gridDim.x;
 
   uint32_t w[NJ][UMAX][8], bm[NJ][UMAX];
@@ -475,8 +494,8 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
     }
     const uint32_t bmax = block_max_u32<kResThreads>(m, red[j]);
     if (threadIdx.x == 0)
-      __hip_atomic_store(reinterpret_cast<uint64_t *>(args.t[j].partials) + k, (epoch << 16) | bmax,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(args.t[j].slots + k, (epoch << 16) | bmax, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // poll: thread p < nwg watches slot p of every tensor
@@ -487,50 +506,67 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
     a[j] = 0;
     if ((int)threadIdx.x < nwg) pending |= 1u << j;
   }
-  bool done = false;
   while (true) {
     uint64_t sw[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
-      sw[j] = (pending >> j) & 1u
-                  ? load_slot(reinterpret_cast<const uint64_t *>(args.t[j].partials) + threadIdx.x)
-                  : 0;
+      sw[j] = (pending >> j) & 1u ? load_slot(args.t[j].slots + threadIdx.x) : 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
       if (((pending >> j) & 1u) && (sw[j] >> 16) == epoch) {
         a[j] = (uint32_t)(sw[j] & 0xFFFFu);
         pending &= ~(1u << j);
       }
-    if (__syncthreads_and(pending == 0)) {
-      done = true;
-      break;
-    }
+    if (__syncthreads_and(pending == 0)) break;
     if (__syncthreads_or(__builtin_amdgcn_s_memrealtime() > deadline)) break;
     __builtin_amdgcn_s_sleep(1);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0)  // every workgroup has read the old word
-    __hip_atomic_store(eword, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // Every thread left the poll loop through a barrier, after its last read of
-  // red[] in the publish step, so red[] can be written again without one; the
-  // NJ tensors' maxima are folded behind a single barrier.  `done` is uniform.
+  // Arrival: every thread of this workgroup read the control word before the
+  // barrier that ended the poll, so no workgroup can see it advanced during
+  // this call.
+  if (threadIdx.x == 0) {
+    const uint64_t before = __hip_atomic_fetch_add(ctrl + 1, uint64_t(1), __ATOMIC_ACQ_REL,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (before == uint64_t(nwg - 1)) {
+      __hip_atomic_store(ctrl + 1, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctrl, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // Fold the slots seen and note the unseen ones, behind one barrier.  Every
+  // thread left the poll loop through a barrier, after its last read of red[]
+  // in the publish step, so red[] can be written again without one.
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const uint32_t m = wave_max_u32(a[j]);
+    const uint64_t mb = __ballot(((pending >> j) & 1u) != 0u);
+    if (lane == 0) {
+      red[j][wv] = m;
+      miss[j][wv] = mb;
+    }
+  }
+  __syncthreads();
   uint32_t A[NJ];
-  if (done) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint32_t m = wave_max_u32(a[j]);
-      if ((threadIdx.x & 63) == 0) red[j][threadIdx.x >> 6] = m;
+  for (int j = 0; j < NJ; ++j) {
+    uint32_t r = red[j][0];
+    uint64_t any = miss[j][0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      r = r > red[j][w] ? r : red[j][w];
+      any |= miss[j][w];
     }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      uint32_t r = red[j][0];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) r = r > red[j][w] ? r : red[j][w];
-      A[j] = r;
+    if (any != 0) {        // the wait expired: read the missing shares directly
+      uint32_t md = 0;
+      for (int w = 0; w < NW; ++w)
+        for (uint64_t mb = miss[j][w]; mb != 0; mb &= mb - 1) {
+          const uint32_t v = share_max<STREAM>(args.t[j], 64 * w + __builtin_ctzll(mb), u, nwg);
+          md = md > v ? md : v;
+        }
+      const uint32_t rd = block_max_u32<kResThreads>(md, red2[j]);
+      r = r > rd ? r : rd;
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) A[j] = tensor_max_direct<kResThreads>(args.t[j], red[j]);
+    A[j] = r;
   }
 
 #pragma unroll
@@ -648,7 +684,7 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
   const int64_t nb = 2 * max_units;                         // 16-element blocks per tensor
   int64_t nwg = (nb + kResThreads - 1) / kResThreads;
   if (nwg > lim.cus) nwg = lim.cus;
-  if (nwg > kResidentSlots) nwg = kResidentSlots;
+  if (nwg > kResidentSlots) nwg = kResidentSlots;       // one polling thread per slot
   const int64_t u = (nb + nwg * kResThreads - 1) / (nwg * kResThreads);
   int li = 0;
   while (li < 4 && (1 << li) < u) ++li;
@@ -703,13 +739,14 @@ static int encode_blocks(int64_t units) {
 
 uint64_t set_resident_wait_ticks(uint64_t ticks) { return g_wait_ticks.exchange(ticks); }
 
-hipError_t launch_encode_from_partials(const QuantJob &job, int64_t nparts, hipStream_t stream) {
+hipError_t launch_encode_from_partials(const QuantJob &job, const uint32_t *maxima, int64_t nparts,
+                                       hipStream_t stream) {
   QuantArgs a{};
   a.t[0].x = job.x;
   a.t[0].codes = job.codes;
   a.t[0].scales = reinterpret_cast<uint16_t *>(job.scales);
   a.t[0].gscale = job.gscale;
-  a.t[0].partials = job.partials;
+  a.t[0].partials = const_cast<uint32_t *>(maxima);
   a.t[0].units = job.rows * (job.cols / 32);
   a.t[0].units_per_row = (uint32_t)(job.cols / 32);
   a.t[0].ld = job.ld;
@@ -729,7 +766,9 @@ hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
     a.t[i].codes = jobs[i].codes;
     a.t[i].scales = reinterpret_cast<uint16_t *>(jobs[i].scales);
     a.t[i].gscale = jobs[i].gscale;
-    a.t[i].partials = jobs[i].partials;
+    uint8_t *scratch = static_cast<uint8_t *>(jobs[i].scratch);
+    a.t[i].slots = reinterpret_cast<uint64_t *>(scratch);
+    a.t[i].partials = reinterpret_cast<uint32_t *>(scratch + kPartialsOffset);
     a.t[i].units = jobs[i].rows * (jobs[i].cols / 32);
     a.t[i].units_per_row = (uint32_t)(jobs[i].cols / 32);
     a.t[i].ld = jobs[i].ld;

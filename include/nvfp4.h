@@ -78,11 +78,14 @@ extern "C" {
  * Workspace bytes nvfp4_quantize needs for an [M, K] input (scratch for the
  * tensor-amax reduction).  Writes *bytes; the size depends only on M and K.
  *
- * Workspaces of every call (quantise, linear, KV append) may hold anything on
- * first use.  The library keeps a call counter in them from one call to the
- * next, in device memory, so calls captured in a HIP graph stay correct on
- * every replay.  Calls that may run at the same time need separate
- * workspaces.
+ * Workspaces of every call (quantise, linear, linear_q, KV append) must be
+ * all zero before their first use (hipMemset, or a zero-filled tensor); after
+ * that only the library writes them, and the caller must not change them
+ * between calls.  The library keeps a call counter in them from one call to
+ * the next, in device memory, so calls captured in a HIP graph stay correct on
+ * every replay.  A workspace may be shared by calls of any kind and size that
+ * are ordered on one stream; calls that may run at the same time need
+ * separate workspaces.
  */
 int nvfp4_quantize_workspace(int64_t M, int64_t K, size_t *bytes);
 
@@ -260,15 +263,6 @@ int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, 
  */
 int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1,
                      uint16_t *K_out, uint16_t *V_out, void *stream);
-
-/*
- * Testing hook, process-wide: the single-launch quantiser's bounded wait for
- * the other workgroups' maxima, in ticks of the GPU's 100 MHz real-time
- * counter (default 100000 = 1 ms).  Returns the previous value.  0 makes every
- * workgroup take the fallback that reads the whole tensor itself; the bytes
- * written are the same either way.  Affects launches made after the call.
- */
-uint64_t nvfp4_testing_set_quantize_wait(uint64_t ticks);
 
 /* Human-readable name of a status code (static storage). */
 const char *nvfp4_strerror(int status);

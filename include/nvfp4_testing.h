@@ -1,0 +1,29 @@
+/*
+ * nvfp4_testing.h — testing hooks of the NVFP4 library (not for production
+ * use; declared apart from the interface in nvfp4.h).
+ */
+#ifndef NVFP4_TESTING_H
+#define NVFP4_TESTING_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Process-wide: the single-launch quantiser's bounded wait for the other
+ * workgroups' maxima, in ticks of the GPU's 100 MHz real-time counter (default
+ * 100000 = 1 ms).  Returns the previous value.  With 0, each workgroup waits
+ * for at most one poll of the other workgroups' slots and reads the shares of
+ * those it has not heard from itself; the bytes written are the same either
+ * way.  Affects launches made after the call.  This exercises, from the host,
+ * the path a workgroup takes when the grid is not resident all at once.
+ */
+uint64_t nvfp4_testing_set_quantize_wait(uint64_t ticks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_TESTING_H */

@@ -27,7 +27,7 @@ def test_quantize_graph_replays(M, K):
     codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
     g = torch.empty((1,), dtype=torch.float32, device=x.device)
-    ws = torch.empty((nv.quantize_workspace_bytes(M, K),), dtype=torch.uint8, device=x.device)
+    ws = nv.workspace(nv.quantize_workspace_bytes(M, K), x.device)
     nv.quantize_into(x, codes, scales, g, ws)                 # warm-up outside the capture
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -51,11 +51,11 @@ def test_linear_and_linear_q_graph_replays():
     wq = nv.quantize(bf16_to_dev(workloads.random_matrix(70, N, K, 0.02)))
     x = bf16_to_dev(xs[0])
     out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    lws = torch.empty((nv.linear_workspace_bytes(M, K),), dtype=torch.uint8, device=x.device)
+    lws = nv.workspace(nv.linear_workspace_bytes(M, K), x.device)
     hq = (torch.empty((M, N // 2), dtype=torch.uint8, device=x.device),
           torch.empty((M, N // 16), dtype=torch.uint8, device=x.device),
           torch.empty((1,), dtype=torch.float32, device=x.device))
-    qws = torch.empty((nv.linear_q_workspace_bytes(M, N, K),), dtype=torch.uint8, device=x.device)
+    qws = nv.workspace(nv.linear_q_workspace_bytes(M, N, K), x.device)
     nv.linear(x, *wq, gelu=True, out=out, ws=lws)
     nv.linear_q(x, *wq, gelu=True, out=hq, ws=qws)
     torch.cuda.synchronize()

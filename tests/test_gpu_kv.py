@@ -147,3 +147,28 @@ def test_many_chunks_dequant():
     assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
     rk2, rv2 = ref.dequant(1234, 1300)
     assert np.array_equal(to_bits(k2), rk2) and np.array_equal(to_bits(v2), rv2)
+
+
+def test_dequant_hand_example_non_power_of_two_scale(golden):
+    # the hand-worked case where fl32(E2M1·S)·g lands on a bf16 tie: the GPU
+    # append gives the fixture's g, scale byte and codes, and its dequant the
+    # fixture's two-rounding result (not one rounding, not the other association)
+    g = golden("kv_dequant_hand_example.txt")
+    x = np.zeros(32, np.float32)
+    x[0] = oracle.bf16_bits_to_f32(np.array([int(g["amax_bits"][0], 16)], np.uint16))[0]
+    m, e = (int(v) for v in g["block_amax"])
+    x[16] = np.ldexp(np.float32(m), e)
+    m, e = (int(v) for v in g["element"])
+    x[17] = np.ldexp(np.float32(m), e)
+    x[18] = -x[17]
+    k = workloads.to_bf16_bits(x).reshape(1, 1, 32)
+    announce("kv dequant hand-worked example")
+    kv = nv.KVCache(4, 1, 32, max_chunks=2)
+    kv.append(bf16_to_dev(k), bf16_to_dev(k))
+    ko, vo = kv.dequant(0, 1)
+    torch.cuda.synchronize()
+    assert to_np(kv.gscale)[0, 0].view(np.uint32) == int(g["g_bits"][0], 16)
+    assert to_np(kv.k_scales)[0, 0, 1] == int(g["scale_byte"][0], 16)
+    kb = to_bits(ko)
+    assert kb[0, 0, 17] == int(g["expected"][0], 16) and kb[0, 0, 18] == int(g["expected_negative"][0], 16)
+    assert np.array_equal(to_bits(vo), kb)

@@ -176,3 +176,127 @@ def test_bounded_wait_fallback_gives_the_same_bytes():
     finally:
         L.nvfp4_testing_set_quantize_wait(prev)
     assert L.nvfp4_testing_set_quantize_wait(prev) == prev
+
+
+# ----------------------------------------------------------------------------
+# The slot protocol of the single-launch quantiser on one reused workspace.
+# Layout of a quantiser workspace (kernels.h): 64-bit slots from byte 0, the
+# control words (last completed epoch, arrival counter) at byte 8192.
+
+SLOTS_BYTES, CTRL_OFFSET = 8192, 8192
+
+
+def _into(x_dev, ws):
+    M, K = x_dev.shape
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x_dev.device)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x_dev.device)
+    g = torch.empty((1,), dtype=torch.float32, device=x_dev.device)
+    nv.quantize_into(x_dev, codes, scales, g, ws)
+    return codes, scales, g
+
+
+def _assert_oracle(x_bits, out, label):
+    rc, rs, rg = oracle.quantize(x_bits)
+    codes, scales, g = out
+    assert to_np(g)[0] == rg, (label, to_np(g)[0], rg)
+    assert np.array_equal(to_np(scales), rs), label
+    assert np.array_equal(to_np(codes), rc), label
+
+
+@pytest.mark.parametrize("M,K", [(1024, 3072), (4096, 3072), (40, 256)])
+def test_expired_wait_then_normal_wait_same_workspace(M, K):
+    # A call whose waits all expire followed by a call with the normal wait on
+    # smaller data, on one workspace, repeated: every call bit-exact.  (An
+    # earlier protocol advanced the epoch word from workgroup 0 after an
+    # expired wait, so a late workgroup could tag its slot with the next call's
+    # epoch and the next call could take that stale maximum.)
+    announce(f"expired wait then normal wait, {M}x{K}")
+    big = workloads.random_matrix(91, M, K, sigma=4.0, outliers=True)
+    small = workloads.random_matrix(92, M, K, sigma=0.25)
+    ws = nv.workspace(nv.quantize_workspace_bytes(M, K))
+    L = nv.lib()
+    dbig, dsmall = bf16_to_dev(big), bf16_to_dev(small)
+    prev = L.nvfp4_testing_set_quantize_wait(0)
+    L.nvfp4_testing_set_quantize_wait(prev)
+    try:
+        for rep in range(6):
+            L.nvfp4_testing_set_quantize_wait(0)
+            o1 = _into(dbig, ws)
+            L.nvfp4_testing_set_quantize_wait(prev)
+            o2 = _into(dsmall, ws)
+            torch.cuda.synchronize()
+            _assert_oracle(big, o1, f"rep {rep} wait 0")
+            _assert_oracle(small, o2, f"rep {rep} normal wait")
+    finally:
+        L.nvfp4_testing_set_quantize_wait(prev)
+
+
+def test_kv_append_expired_wait_then_normal_wait():
+    H, D, T = 24, 128, 200
+    rng = np.random.default_rng(93)
+    L = nv.lib()
+    prev = L.nvfp4_testing_set_quantize_wait(0)
+    L.nvfp4_testing_set_quantize_wait(prev)
+    kv = nv.KVCache(T * 8, H, D, max_chunks=8)
+    ref = oracle.KVCacheRef(T * 8, H, D)
+    announce("kv append: expired wait then normal wait, one workspace")
+    try:
+        for rep in range(8):
+            scale = 8.0 if rep % 2 == 0 else 0.125
+            k = workloads.to_bf16_bits(scale * rng.standard_normal((T, H, D)).astype(np.float32))
+            v = workloads.to_bf16_bits(scale * 3 * rng.standard_normal((T, H, D)).astype(np.float32))
+            L.nvfp4_testing_set_quantize_wait(0 if rep % 2 == 0 else prev)
+            kv.append(bf16_to_dev(k), bf16_to_dev(v))
+            ref.append(k, v)
+        torch.cuda.synchronize()
+    finally:
+        L.nvfp4_testing_set_quantize_wait(prev)
+    n = kv.n_tokens
+    assert np.array_equal(to_np(kv.k_codes)[:n], ref.k_codes[:n])
+    assert np.array_equal(to_np(kv.v_codes)[:n], ref.v_codes[:n])
+    assert np.array_equal(to_np(kv.k_scales)[:n], ref.k_scales[:n])
+    assert np.array_equal(to_np(kv.v_scales)[:n], ref.v_scales[:n])
+    assert np.array_equal(to_np(kv.gscale), np.array(ref.gscale, dtype=np.float32).reshape(-1, 2))
+
+
+def test_stale_slots_of_earlier_calls_are_ignored():
+    # A workspace in a state earlier calls leave behind: the control word at
+    # epoch E, every slot tagged E or below and holding the largest finite
+    # bf16 magnitude.  A call on small data must not take any of them.
+    M, K = 2048, 3072
+    x = workloads.random_matrix(94, M, K, sigma=0.5)
+    ws = nv.workspace(nv.quantize_workspace_bytes(M, K))
+    E = 0x123456789A
+    slots = np.zeros(SLOTS_BYTES // 8, dtype=np.uint64)
+    slots[0::2] = np.uint64((E << 16) | 0x7F7F)
+    slots[1::2] = np.uint64(((E - 1) << 16) | 0x7F7F)
+    ws[:SLOTS_BYTES].copy_(torch.from_numpy(slots.view(np.uint8)))
+    ws[CTRL_OFFSET:CTRL_OFFSET + 8].copy_(torch.from_numpy(np.array([E], np.uint64).view(np.uint8)))
+    announce("stale slots tagged with the last completed epoch")
+    for rep in range(3):
+        out = _into(bf16_to_dev(x), ws)
+        torch.cuda.synchronize()
+        _assert_oracle(x, out, f"rep {rep}")
+    ctrl = to_np(ws[CTRL_OFFSET:CTRL_OFFSET + 16]).view(np.uint64)
+    assert ctrl[0] == E + 3 and ctrl[1] == 0          # three calls completed, no arrival pending
+
+
+def test_workspace_shared_by_every_kind_of_call():
+    # one workspace used in turn by the single-launch path, the streamed path,
+    # the two-launch 2-D path and the adaptive mode, each bit-exact
+    ws = nv.workspace(nv.quantize_workspace_bytes(1, 32))
+    cases = [(workloads.random_matrix(95, 3000, 3072, 1.0, True), {}),
+             (workloads.random_matrix(96, 11000, 3072, 1.0, True), {}),
+             (workloads.random_matrix(97, 512, 1024, 0.02), {"blocks2d": True}),
+             (workloads.random_matrix(98, 3000, 3072, 0.5, True), {"adaptive46": True}),
+             (workloads.random_matrix(99, 64, 256, 2.0), {})]
+    for i, (x, kw) in enumerate(cases):
+        announce(f"shared workspace, call {i} shape={x.shape} {kw}")
+        M, K = x.shape
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device="cuda")
+        g = torch.empty((1,), dtype=torch.float32, device="cuda")
+        nv.quantize_into(bf16_to_dev(x), codes, scales, g, ws, **kw)
+        torch.cuda.synchronize()
+        rc, rs, rg = oracle.quantize(x, **kw)
+        assert to_np(g)[0] == rg and np.array_equal(to_np(scales), rs) and np.array_equal(to_np(codes), rc), i
