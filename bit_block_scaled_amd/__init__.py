@@ -19,6 +19,7 @@ import torch
 from ._lib import (  # noqa: F401
     LIB_PATH,
     NVFP4_EPI_GELU_TANH,
+    NVFP4_NOALLOC_MAX_ELEMENTS,
     NVFP4_Q_ADAPTIVE_4_6,
     NVFP4_Q_BLOCK_2D,
     NVFP4_TILES,
@@ -29,7 +30,7 @@ from ._lib import (  # noqa: F401
     lib,
 )
 
-__all__ = ["quantize", "quantize_into", "gemm", "linear", "linear_q", "KVCache", "NVFP4Error", "lib",
+__all__ = ["quantize", "quantize_into", "gemm", "linear", "linear_noalloc", "linear_q", "KVCache", "NVFP4Error", "lib",
            "gemm_tile", "workspace", "quantize_workspace_bytes", "linear_workspace_bytes",
            "linear_q_workspace_bytes"]
 
@@ -157,6 +158,28 @@ def linear(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, ws=None, tile=None):
     flags = _flags(gelu, tile)
     check(lib().nvfp4_linear(_ptr(x), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias), _ptr(out),
                              M, N, K, flags, _ptr(ws), ws.numel(), _stream(x.device)))
+    return out
+
+
+def linear_noalloc(x, Wq, Ws, Wg, bias=None, gelu=False, out=None, tile=None):
+    """nvfp4_linear_noalloc: the W4A4 linear layer with the library's built-in
+    device workspace (no workspace argument, nothing allocated by the library;
+    ``out`` may be passed so that this call allocates nothing either).  Calls
+    that may overlap on one device race; M·K <= NVFP4_NOALLOC_MAX_ELEMENTS."""
+    M, K = x.shape
+    N = Wq.shape[0]
+    _need(x, torch.bfloat16, "x")
+    _need(Wq, torch.uint8, "Wq", (N, K // 2))
+    _need(Ws, torch.uint8, "Ws", (N, K // 16))
+    _need(Wg, torch.float32, "Wg", (1,))
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias", (N,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, torch.bfloat16, "out", (M, N))
+    flags = _flags(gelu, tile)
+    check(lib().nvfp4_linear_noalloc(_ptr(x), _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias), _ptr(out),
+                                     M, N, K, flags, _stream(x.device)))
     return out
 
 

@@ -22,6 +22,7 @@ NVFP4_EWORKSPACE = 2
 NVFP4_ECAPACITY = 3
 NVFP4_EHIP = 4
 NVFP4_EPI_GELU_TANH = 0x1
+NVFP4_NOALLOC_MAX_ELEMENTS = 1 << 26
 NVFP4_Q_ADAPTIVE_4_6 = 0x10
 NVFP4_Q_BLOCK_2D = 0x20
 NVFP4_TILES = {(256, 256): 0x100, (256, 192): 0x200, (192, 256): 0x300, (256, 128): 0x400,
@@ -51,6 +52,7 @@ _SIGS = {
     "nvfp4_gemm_tile": ([_i64, _i64, _i64, C.POINTER(C.c_int), C.POINTER(C.c_int)], C.c_int),
     "nvfp4_linear_workspace": ([_i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_linear": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, C.c_uint32, _p, _sz, _p], C.c_int),
+    "nvfp4_linear_noalloc": ([_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, C.c_uint32, _p], C.c_int),
     "nvfp4_linear_q_workspace": ([_i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_linear_q": ([_p, _p, _p, _p, _p, _i64, _i64, _i64, C.c_uint32, _p, _p, _p, _p, _sz, _p],
                        C.c_int),

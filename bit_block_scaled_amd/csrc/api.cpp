@@ -8,6 +8,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <string>
 
 #include "kernels.h"
@@ -175,6 +176,48 @@ int nvfp4_linear(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const 
   return hip_status(nvfp4::launch_gemm(a, st), "linear/gemm");
 }
 
+// ---------------------------------------------------------------------------
+// nvfp4_linear_noalloc: nvfp4_linear with its workspace in a file-scope device
+// array, for callers that cannot allocate.  Layout (fixed, so the quantiser's
+// call counter stays in place from one call to the next):
+//   [0, kNoAllocMaxElements/2)            activation codes
+//   [.., + kNoAllocMaxElements/16)        activation block scales
+//   [.., + 256)                           activation tensor scale
+//   [.., + kQuantScratchBytes)            quantiser scratch
+// The array is zero when the code object is loaded, which is the state the
+// quantiser scratch needs before its first use; the library keeps it valid.
+constexpr size_t kNoAllocCodes = 0;
+constexpr size_t kNoAllocScales = kNoAllocCodes + size_t(NVFP4_NOALLOC_MAX_ELEMENTS) / 2;
+constexpr size_t kNoAllocGscale = kNoAllocScales + size_t(NVFP4_NOALLOC_MAX_ELEMENTS) / 16;
+constexpr size_t kNoAllocQuant = kNoAllocGscale + 256;
+constexpr size_t kNoAllocBytes = kNoAllocQuant + kQuantWs;
+static_assert(kNoAllocScales % 256 == 0 && kNoAllocGscale % 256 == 0, "aligned regions");
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device holds its own copy of the array).  In host code the
+// array's name stands for a host-side shadow, never for device memory.
+static std::atomic<uintptr_t> g_scratch_addr[64];
+
+static int noalloc_scratch(uint8_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "linear_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(NVFP4_EINVAL, "linear_noalloc: device index beyond 63");
+  uintptr_t a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (a == 0) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "linear_noalloc: hipGetSymbolAddress");
+    if (p == nullptr) return fail(NVFP4_EHIP, "linear_noalloc: no device address for the scratch array");
+    a = reinterpret_cast<uintptr_t>(p);
+    g_scratch_addr[dev].store(a, std::memory_order_release);
+  }
+  *out = reinterpret_cast<uint8_t *>(a);
+  return NVFP4_OK;
+}
+
 // nvfp4_linear_q workspace: [linear workspace | tile maxima | H bf16 [M, N]]
 struct LinearQWs {
   LinearWs lin;
@@ -190,6 +233,28 @@ static LinearQWs linear_q_ws(int64_t M, int64_t N, int64_t K) {
   w.h = round_up(w.slots + size_t(w.max_tiles) * sizeof(uint32_t), 256);
   w.total = round_up(w.h + size_t(M) * size_t(N) * sizeof(uint16_t), 256);
   return w;
+}
+
+int nvfp4_linear_noalloc(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const float *Wg,
+                         const uint16_t *bias, uint16_t *C, int64_t M, int64_t N, int64_t K,
+                         uint32_t flags, void *stream) {
+  int s = check_gemm_args(nullptr, nullptr, nullptr, Wq, Ws, Wg, bias, C, M, N, K, flags, false);
+  if (s) return s;
+  if ((s = check_ptr(x, "x"))) return s;
+  if (M > NVFP4_NOALLOC_MAX_ELEMENTS / K)
+    return fail(NVFP4_EINVAL, "linear_noalloc: M*K = " + std::to_string(M * K) +
+                                  " exceeds the built-in workspace (NVFP4_NOALLOC_MAX_ELEMENTS = " +
+                                  std::to_string(int64_t(NVFP4_NOALLOC_MAX_ELEMENTS)) + ")");
+  uint8_t *base = nullptr;
+  if ((s = noalloc_scratch(&base))) return s;
+  uint8_t *aq = base + kNoAllocCodes;
+  uint8_t *as = base + kNoAllocScales;
+  float *ag = reinterpret_cast<float *>(base + kNoAllocGscale);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  nvfp4::QuantJob j{x, aq, as, ag, base + kNoAllocQuant, M, K, K};
+  if ((s = hip_status(nvfp4::launch_quantize(&j, 1, st), "linear_noalloc/quantize"))) return s;
+  nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, C, M, N, K, flags};
+  return hip_status(nvfp4::launch_gemm(a, st), "linear_noalloc/gemm");
 }
 
 int nvfp4_linear_q_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes) {

@@ -179,6 +179,31 @@ int nvfp4_linear_q(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, cons
                    uint8_t *Hq, uint8_t *Hs, float *Hg, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Largest activation (M·K elements) nvfp4_linear_noalloc accepts: its built-in
+ * workspace holds the NVFP4 activation of that size (36 MiB per device).
+ */
+#define NVFP4_NOALLOC_MAX_ELEMENTS (1LL << 26)
+
+/*
+ * nvfp4_linear without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, arithmetic and bytes as
+ * nvfp4_linear; the quantised activation and the quantiser's scratch live in
+ * an array of the library's own device memory (one per device, zero at load,
+ * held until the process ends).  Calls nothing that allocates.
+ *   Requires M·K <= NVFP4_NOALLOC_MAX_ELEMENTS (else NVFP4_EINVAL, with the
+ *   limit in the message), besides nvfp4_linear's conditions.
+ *   Every call on one device shares that device's array: calls that may
+ *   overlap on one device (different streams without ordering) race and give
+ *   undefined results.  Calls ordered on one stream are safe in any sequence
+ *   of sizes.
+ */
+int nvfp4_linear_noalloc(const uint16_t *x,
+                         const uint8_t *Wq, const uint8_t *Ws, const float *Wg,
+                         const uint16_t *bias, uint16_t *C,
+                         int64_t M, int64_t N, int64_t K, uint32_t flags, void *stream);
+
+/*
  * Workgroup tile (rows of A x rows of W) nvfp4_gemm uses for an M x N x K
  * problem; informational (for reporting), enqueues nothing.
  */

@@ -206,3 +206,16 @@ def test_linear_q_rejects(L):
     assert L.nvfp4_linear_q(*args, 64, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, 16, None) == EWS
     assert L.nvfp4_linear_q(*args, 64, 64, 64, 0x80, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
     assert L.nvfp4_linear_q(*args, 64, 64, 64, 0, MIS, FAKE, FAKE, FAKE, 1 << 30, None) == EINVAL
+
+
+def test_linear_noalloc_rejects(L):
+    # argument errors and the size limit of the built-in workspace are found on
+    # the host, before the device array is looked up or anything is enqueued
+    f = L.nvfp4_linear_noalloc
+    lim = _lib.NVFP4_NOALLOC_MAX_ELEMENTS
+    assert f(None, FAKE, FAKE, FAKE, None, FAKE, 64, 64, 64, 0, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, MIS, FAKE, 64, 64, 64, 0, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 64, 64, 40, 0, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, lim // 3072 + 1, 64, 3072, 0, None) == EINVAL
+    msg = L.nvfp4_last_error()
+    assert b"NVFP4_NOALLOC_MAX_ELEMENTS" in msg and str(lim).encode() in msg
