@@ -3,11 +3,13 @@ quantisation of the hidden activation H, down projection.
 
 The chain is checked stage by stage.  Each GPU stage takes the oracle's own
 intermediate as its input (never the reverse), so every expected value comes
-from the oracle alone.  A GPU H that differs from the oracle's H in the last
-bf16 bit (GELU's exponential is evaluated differently on the two sides) may
-change a few codes downstream, so the end-to-end GPU chain is compared with a
-looser normwise bound.  The full-size up and down projections are checked on
-sampled rows and columns.
+from the oracle alone.  The all-GPU chain is then compared end to end with the
+oracle's chain, at the same normwise bound as a single GEMM.  A GPU H may
+differ from the oracle's H in the last bf16 bit (the FP32 accumulation order
+and GELU's exponential differ between the two sides); such an element can
+change its code, and only there: the NVFP4 hand-off of H is checked against
+the oracle's quantisation of its own H block by block.  The full-size up and
+down projections are checked on sampled rows and columns.
 """
 
 import numpy as np
@@ -22,7 +24,11 @@ from gpu_helpers import (GEMM_TOL, announce, bf16_to_dev, f32_to_dev, gemm_error
 
 pytestmark = pytest.mark.gpu
 
-CHAIN_TOL = 2e-2          # end to end, GPU intermediates throughout
+# End to end, GPU intermediates throughout: the gate of a single W4A4 GEMM.
+# The chain's output differs from the oracle chain's only through the final
+# bf16 rounding (as for one GEMM) and through the few H codes that flip where
+# H differs in its last bit (at most 0.1 % of the codes, checked below).
+CHAIN_TOL = GEMM_TOL
 
 
 def _upload_q(q):
@@ -67,10 +73,9 @@ def test_ffn_chain_stagewise():
     h = nv.linear(bf16_to_dev(x), *wu_q, gelu=True)
     y = nv.linear(h, *wd_q)
     torch.cuda.synchronize()
-    yb = oracle.bf16_bits_to_f32(to_bits(y)).astype(np.float64)
-    err = np.linalg.norm(yb - y64) / np.linalg.norm(y64)
-    announce(f"  end to end: {err:.3e} vs fp64 chain")
-    assert err <= CHAIN_TOL
+    e_ref, e_64 = gemm_errors(to_bits(y), y64, y_ref)
+    announce(f"  end to end: {e_ref:.3e} vs bf16 oracle chain, {e_64:.3e} vs fp64 chain")
+    assert e_ref <= CHAIN_TOL and e_64 <= CHAIN_TOL
 
 
 def _sampled(x_bits, w_bits, rows, cols, gelu):
@@ -156,3 +161,32 @@ def test_ffn_chain_through_linear_q():
     err = np.linalg.norm(yb - y64) / np.linalg.norm(y64)
     announce(f"  chain through linear_q: {err:.3e} vs fp64 chain")
     assert err <= CHAIN_TOL
+
+
+@pytest.mark.parametrize("M,D,HID,seed", [(256, 512, 2048, 21), (1024, 3072, 4096, 41)])
+def test_linear_q_bytes_against_the_oracle(M, D, HID, seed):
+    # (Hq, Hs, Hg) of the fused hand-off against oracle.quantize of the
+    # oracle's own H: the tensor scale equal, and in every 16-element block
+    # whose H the GPU computed bit for bit like the oracle, the scale byte and
+    # the codes equal; the other blocks (last-bit differences of H) are few
+    announce(f"linear_q bytes vs oracle M={M} D={D} hidden={HID}")
+    x = workloads.random_matrix(seed, M, D, 1.0, outliers=True)
+    qx = oracle.quantize(x)
+    qu = oracle.quantize(workloads.random_matrix(seed + 1, HID, D, 0.02))
+    _, h_ref = oracle.gemm_ref(*qx, *qu, gelu=True)
+    rq, rs, rg = oracle.quantize(h_ref)
+    xd, wd = bf16_to_dev(x), _upload_q(qu)
+    hq, hs, hg = nv.linear_q(xd, *wd, gelu=True)
+    h_gpu = to_bits(nv.linear(xd, *wd, gelu=True))       # the same H the hand-off encodes
+    torch.cuda.synchronize()
+    assert to_np(hg)[0] == rg
+    same_h = (h_gpu == h_ref).reshape(M, HID // 16, 16).all(axis=2)        # per block
+    frac_h = 1.0 - same_h.mean()
+    gq, gs = oracle.unpack_nibbles(to_np(hq)).reshape(M, HID // 16, 16), to_np(hs)
+    oq = oracle.unpack_nibbles(rq).reshape(M, HID // 16, 16)
+    assert np.array_equal(gs[same_h], rs[same_h])
+    assert np.array_equal(gq[same_h], oq[same_h])
+    codes_equal, scales_equal = (gq == oq).mean(), (gs == rs).mean()
+    announce(f"  blocks with a differing H element {frac_h:.2e}; codes equal {codes_equal:.6f}, "
+             f"scales equal {scales_equal:.6f}")
+    assert frac_h < 0.25 and codes_equal >= 0.999 and scales_equal >= 0.999

@@ -1,6 +1,6 @@
 """GPU parity of the NVFP4 KV cache: every append's codes, scales and tensor
 scales bit-exact against the oracle cache, dequant bit-exact against the
-oracle's dequant chain; the full 65536-token workload on sampled chunks."""
+oracle's dequant chain; the full 65536-token workload on every chunk."""
 
 import numpy as np
 import pytest
@@ -69,7 +69,9 @@ def test_capacity_errors_leave_cache_unchanged():
     assert gpu.n_tokens == 10 and gpu.n_chunks == 2
 
 
-def test_full_workload_sampled():
+def test_full_workload_every_chunk():
+    # the 65536-token workload: 74 appends of 880 tokens and one of 416, every
+    # chunk's codes, scales and tensor scales and the whole read-back bit-exact
     K, V, sizes = workloads.kv()
     H, D = workloads.HEADS, workloads.HEAD_DIM
     T = K.shape[0]
@@ -79,29 +81,19 @@ def test_full_workload_sampled():
     starts = np.r_[0, np.cumsum(sizes)]
     for i, n in enumerate(sizes):
         gpu.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]])
-    torch.cuda.synchronize()
-    assert gpu.n_tokens == T and gpu.n_chunks == len(sizes)
-    assert list(to_np(gpu.chunk_start)) == list(starts)
-    # bit-exact on sampled chunks (first, a middle one, the 416-token tail)
-    for ci in (0, 37, len(sizes) - 1):
-        a, b = starts[ci], starts[ci + 1]
-        ref = oracle.KVCacheRef(b - a, H, D)
-        ref.append(K[a:b], V[a:b])
-        assert np.array_equal(to_np(gpu.k_codes)[a:b], ref.k_codes)
-        assert np.array_equal(to_np(gpu.v_codes)[a:b], ref.v_codes)
-        assert np.array_equal(to_np(gpu.k_scales)[a:b], ref.k_scales)
-        assert np.array_equal(to_np(gpu.v_scales)[a:b], ref.v_scales)
-        assert tuple(to_np(gpu.gscale)[ci]) == ref.gscale[0]
-        # dequant of the whole cache, sampled on this chunk
     ko, vo = gpu.dequant(0, T)
     torch.cuda.synchronize()
-    kb, vb = to_bits(ko), to_bits(vo)
-    for ci in (0, 37, len(sizes) - 1):
-        a, b = starts[ci], starts[ci + 1]
-        ref = oracle.KVCacheRef(b - a, H, D)
-        ref.append(K[a:b], V[a:b])
-        rk, rv = ref.dequant(0, b - a)
-        assert np.array_equal(kb[a:b], rk) and np.array_equal(vb[a:b], rv), ci
+    del kd, vd
+    assert gpu.n_tokens == T and gpu.n_chunks == len(sizes)
+    announce("  oracle cache")
+    ref = oracle.KVCacheRef(T, H, D)
+    for i in range(len(sizes)):
+        ref.append(K[starts[i]:starts[i + 1]], V[starts[i]:starts[i + 1]])
+    _compare_cache(gpu, ref, T)
+    announce("  oracle dequant")
+    rk, rv = ref.dequant(0, T)
+    assert np.array_equal(to_bits(ko), rk)
+    assert np.array_equal(to_bits(vo), rv)
     # storage closed form: 9/8 bytes per element for K and V together
     nbytes = sum(t.numel() for t in (gpu.k_codes, gpu.v_codes, gpu.k_scales, gpu.v_scales))
     assert nbytes * 8 == 9 * T * H * D
