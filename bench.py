@@ -1,31 +1,38 @@
 #!/usr/bin/env python3
 """Benchmark of the NVFP4 W4A4 hot path on one MI355X.
 
-One step is one pass of the whole path over one batch of the DiT QKV
-projection workload (X bf16 [4096, 3072] ~ N(0,1) with 0.1 % ×50 outliers,
-W [9216, 3072] ~ N(0, 0.02), bias [9216] ~ N(0, 0.01); seeded synthetic data):
+Headline step: the DiT FFN pair, the largest single-GPU configuration
+(seeded synthetic data, inputs resident in HBM before timing):
 
-  1. nvfp4_quantize   X → NVFP4 codes / E4M3 block scales / FP32 tensor scale
-  2. nvfp4_gemm       W4A4 GEMM against the pre-quantised W, + bias → C bf16
-                      [4096, 9216]  (= the linear layer, quantise + GEMM)
-  3. nvfp4_kv_append  the K and V column slices of C (24 heads x 128) appended
-                      to an NVFP4 KV cache (read in place, token stride 9216)
-  4. nvfp4_kv_dequant those 4096 tokens read back as bf16 K and V
+  X bf16 [8192, 3072] ~ N(0,1) with 0.1 % of entries x50,
+  W_up [14336, 3072] and W_down [3072, 14336] ~ N(0, 0.02), quantised once
+  to NVFP4 before timing (weights are materialised once in 4 bits).
 
-The weights are quantised once before timing (they are materialised once in
-4 bits).  Inputs are resident in HBM before the timed region; the K timed
-steps run back to back on one stream, bracketed by device synchronisation.
+  1. nvfp4_linear_q  quantise X per call -> W4A4 GEMM with the GELU-tanh
+                     epilogue -> H [8192, 14336] handed on in NVFP4 (the
+                     encoder folds the GEMM's per-tile output maxima, H is
+                     read once)
+  2. nvfp4_gemm      H (NVFP4) x W_down -> Y bf16 [8192, 3072]
 
-Printed: one JSON line.  `value` is 2·M·N·K per step over the step time
-(TFLOP/s of the linear layer, with the quantiser and the KV append/dequant
-inside the step time).  `roofline` is for the dominant kernel (the GEMM),
-timed with HIP events on the stream it runs on.  `cpu_baseline` is the CPU
-oracle on a bounded sample of the same workload.
+`value` = 2 * (2*M*N*K) per step / step time (TFLOP/s): the step is captured
+once in a HIP graph, W replays untimed, then exactly K replays between two
+device synchronisations.  The same step is also run eagerly K times with an
+event after every kernel (the library's launch-event testing hook), which
+gives the per-kernel breakdown and the dominant kernel's roofline (the up
+GEMM).  Further entries in `kernels` time the other configurations' kernels
+(QKV and long-context GEMMs and quantisers, the 65536-token KV append
+sequence and its read-back, a 1 GiB device copy) with p10/p50/p90 over
+repetitions; the HBM-bound ones after a 1 GiB cache flush ("cold").
+`cpu_baseline` is the CPU oracle on a bounded sample of the FFN step.
+
+Other modes: --copy-only (1 GiB copy, for rocprofv3 counter calibration),
+--gemm-clock (QKV GEMM on benchmark vs constant operands).
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes as C
 import hashlib
 import json
 import os
@@ -38,11 +45,12 @@ if ROOT not in sys.path:
 
 METRIC = "W4A4 NVFP4 GEMM TFLOPS (% MFMA peak) + quantize GB/s (% HBM), 1×MI355X"
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
-PEAK_F16_TFLOPS = 2500.0         # dense fp16/bf16 MFMA
+PEAK_F16_TFLOPS = 2500.0         # dense fp16/bf16 MFMA (the instruction the exact decode feeds)
 PEAK_FP8_TFLOPS = 5000.0
 PEAK_FP4_TFLOPS = 10100.0
-PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_qkv_4096x9216x3072_pmc_traffic.txt")
-# the GEMM kernel and its host dispatch (the traffic counters are valid for these sources only)
+Q_BYTES_PER_ELEM = 2.5625        # 2 B bf16 read + 0.5 B codes + 1/16 B scale
+PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_ffn_up_8192x14336x3072_pmc.txt")
+# the GEMM kernel and its host dispatch (the traffic counters hold for these sources only)
 GEMM_SRC = [os.path.join(ROOT, "bit_block_scaled_amd", "csrc", f) for f in ("gemm_kernel.h", "gemm.hip")]
 
 
@@ -65,33 +73,76 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline step (no other configurations)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
-    ap.add_argument("--extended", metavar="PATH", default=None,
-                    help="also measure the other DiT shapes and the 65536-token KV sequence; "
-                         "write JSON lines to PATH")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--gemm-clock", action="store_true",
                     help="run only the QKV GEMM, 20 launches on the benchmark's operands, then 20 on "
-                         "constant-byte operands (for rocprofv3 --pmc GRBM_GUI_ACTIVE: the clock "
-                         "under load depends on the operand bits)")
+                         "constant-byte operands (for rocprofv3 --pmc GRBM_GUI_ACTIVE)")
     return ap.parse_args()
 
 
-class Timer:
-    """HIP events recorded on the current (work) stream."""
-
-    def __init__(self, torch, n):
-        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
-        self.i = 0
-
-    def mark(self):
-        self.ev[self.i].record()
-        self.i += 1
+def pct(samples):
+    """p10 / p50 / p90 / mean of a list of microsecond samples."""
+    import numpy as np
+    a = np.asarray(samples, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 2), "p50": round(float(np.percentile(a, 50)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "mean": round(float(a.mean()), 2), "n": int(a.size)}
 
 
-def cpu_baseline(w, qw_oracle, seconds):
-    """The oracle as it stands, on a sample of the step's rows."""
+def roof_gemm(flops, us):
+    t = flops / us / 1e6
+    return {"bound": "mfma", "achieved": round(t, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(t / PEAK_F16_TFLOPS, 4), "frac_fp8_peak": round(t / PEAK_FP8_TFLOPS, 4),
+            "frac_fp4_peak": round(t / PEAK_FP4_TFLOPS, 4)}
+
+
+def roof_hbm(nbytes, us, copy_gbs=None):
+    g = nbytes / us / 1e3
+    r = {"bound": "hbm", "achieved": round(g, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+         "frac": round(g / PEAK_HBM_GBS, 4), "algorithmic_bytes": nbytes}
+    if copy_gbs:
+        r["frac_of_copy"] = round(g / copy_gbs, 4)
+    return r
+
+
+class CacheFlush:
+    """Evicts L2 and the MALL by reading a 1 GiB buffer (written once here).
+
+    A read leaves only clean lines behind; a written buffer would leave 1 GiB
+    of dirty lines whose write-back competes with the timed kernel's reads."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(7).view(torch.int64)
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        self.buf.max()
+
+
+def time_us(torch, fn, reps, warmup=10, flush=None):
+    """Microseconds of fn() per repetition, from HIP events on the current
+    stream around each call (after a cache flush when `flush` is given)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3)
+    return out
+
+
+def cpu_baseline(w, qu, qd, seconds):
+    """The oracle as it stands, on a sample of the FFN step's rows."""
     import numpy as np
     import oracle
     try:
@@ -100,34 +151,33 @@ def cpu_baseline(w, qw_oracle, seconds):
         threads = max(blas) if blas else 1
     except Exception:      # threadpoolctl missing: numpy's BLAS default
         threads = os.cpu_count() or 1
-    S = 256
-    H, D = 24, 128
-    N, K = w.N, w.K
+    S = 32
+    M, D = w.x.shape
+    HID = w.w.shape[0]
     reps, t_total = 0, 0.0
     while reps == 0 or t_total < seconds:
         t0 = time.perf_counter()
         A = np.abs(oracle.bf16_bits_to_f32(w.x)).max()                   # tensor amax over all of X
         qa = oracle.quantize(w.x[:S], amax=A)
-        _, cref = oracle.gemm_ref(*qa, *qw_oracle, bias_bits=w.bias)
-        kv = oracle.KVCacheRef(S, H, D)
-        kv.append(np.ascontiguousarray(cref[:, 3072:6144]).reshape(S, H, D),
-                  np.ascontiguousarray(cref[:, 6144:9216]).reshape(S, H, D))
-        kv.dequant(0, S)
+        _, h = oracle.gemm_ref(*qa, *qu, gelu=True)                      # up GEMM + GELU, bf16 H rows
+        qh = oracle.quantize(h)                                          # H's amax over the sampled rows
+        oracle.gemm_ref(*qh, *qd)                                        # down GEMM
         t_total += time.perf_counter() - t0
         reps += 1
-        if reps >= 50:
+        if reps >= 20:
             break
-    tflops = 2.0 * S * N * K * reps / t_total / 1e12
+    tflops = 4.0 * S * HID * D * reps / t_total / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"{S} of {w.M} rows of the QKV step, {reps} reps in {t_total:.1f} s: tensor amax "
-                       f"over all of X, NVFP4 quantise of the sampled rows, FP64 GEMM against the full "
-                       f"pre-quantised W + bias with bf16 rounding, KV append + dequant of their K/V; "
-                       f"host has {os.cpu_count()} logical CPUs, BLAS threads {threads}")}
+            "sample": (f"{S} of {M} rows of the FFN step, {reps} reps in {t_total:.1f} s: tensor amax over "
+                       f"all of X, NVFP4 quantise of the sampled rows, FP64 up GEMM against the full "
+                       f"pre-quantised W_up with GELU and bf16 rounding, NVFP4 quantise of those H rows "
+                       f"(their own amax), FP64 down GEMM against the full pre-quantised W_down; host has "
+                       f"{os.cpu_count()} logical CPUs, BLAS threads {threads}")}
 
 
 def pmc_traffic():
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary
-    (its `key: value` lines), or None when absent or taken on a different GEMM
+    """HBM bytes per up-GEMM launch from the committed rocprofv3 counter summary
+    (its `key: value` lines), or None when absent or taken on another GEMM
     source."""
     if not os.path.exists(PROFILE_PMC):
         return None
@@ -147,8 +197,8 @@ def pmc_traffic():
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (this build has "
-              f"no multi-GPU path; run with --gpus 1)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (the path runs on one "
+              f"GPU; run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -161,6 +211,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    L = nv.lib()
 
     if a.copy_only:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -174,86 +225,59 @@ def main():
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    log("generating the QKV workload (seed 1)")
-    w = workloads.qkv()
-    M, K, N = w.M, w.K, w.N
-    HD = 3072
-    x, W, bias = up(w.x), up(w.w), up(w.bias)
-    wq, wsc, wg = nv.quantize(W)                           # offline weight quantisation
-    aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
-    asc = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
-    ag = torch.empty((1,), dtype=torch.float32, device=dev)
-    qws = nv.workspace(nv.quantize_workspace_bytes(M, K), dev)
-    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    kv = nv.KVCache(M, 24, 128, max_chunks=1, device=dev)
-    k_out = torch.empty((M, 24, 128), dtype=torch.bfloat16, device=dev)
-    v_out = torch.empty_like(k_out)
-    Kv, Vv = C[:, HD:2 * HD], C[:, 2 * HD:3 * HD]
-    torch.cuda.synchronize()
-
     if a.gemm_clock:
-        nv.quantize_into(x, aq, asc, ag, qws)
-        res = {}
-        for kind in ("benchmark", "constant"):
-            if kind == "constant":              # fixed byte patterns, every element alike
-                aq.fill_(0x35); wq.fill_(0x53); asc.fill_(0x38); wsc.fill_(0x30)
-            for _ in range(3):
-                nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, out=C)
-            ts = Timer(torch, 21)
-            for _ in range(20):
-                ts.mark()
-                nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, out=C)
-            ts.mark()
-            torch.cuda.synchronize()
-            res[kind + "_us"] = float(np.mean([ts.ev[i].elapsed_time(ts.ev[i + 1]) * 1e3 for i in range(20)]))
-        print(json.dumps({"gemm_clock": res, "launches_per_kind": 20, "warmup_per_kind": 3}))
+        gemm_clock(a, nv, torch, np, workloads, dev, up)
         return
 
-    def step(t=None):
-        if t: t.mark()
-        nv.quantize_into(x, aq, asc, ag, qws)
-        if t: t.mark()
-        nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, out=C)
-        if t: t.mark()
-        kv.reset()
-        kv.append(Kv, Vv)
-        if t: t.mark()
-        kv.dequant(0, M, k_out, v_out)
-        if t: t.mark()
+    # ------------------------------------------------------------------ FFN step
+    log("generating the FFN workload (seed 2)")
+    w = workloads.ffn()
+    M, D = w.x.shape
+    HID = w.w.shape[0]
+    x = up(w.x)
+    Wu, Wd = up(w.w), up(w.w2)
+    qu, qd = nv.quantize(Wu), nv.quantize(Wd)              # offline weight quantisation
+    del Wu, Wd
+    hq = torch.empty((M, HID // 2), dtype=torch.uint8, device=dev)
+    hs = torch.empty((M, HID // 16), dtype=torch.uint8, device=dev)
+    hg = torch.empty((1,), dtype=torch.float32, device=dev)
+    Y = torch.empty((M, D), dtype=torch.bfloat16, device=dev)
+    lq_ws = nv.workspace(nv.linear_q_workspace_bytes(M, HID, D), dev)
+    torch.cuda.synchronize()
+
+    def step():
+        nv.linear_q(x, *qu, gelu=True, out=(hq, hs, hg), ws=lq_ws)
+        nv.gemm(hq, hs, hg, *qd, out=Y)
 
     log(f"warmup {a.warmup} steps")
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
 
-    # --- eager launches, K steps with events between the calls of every step
-    #     (per-call breakdown and the GEMM's roofline)
-    timer = Timer(torch, 5 * a.steps)
-    log(f"timing {a.steps} eager steps")
+    # eager steps: an event before the step and one after each of its four
+    # kernels (quantise X, up GEMM, encode H, down GEMM)
+    log(f"timing {a.steps} eager steps (per-kernel events)")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(a.steps)]
+    for row in evs:
+        for e in row:
+            e.record()
     torch.cuda.synchronize()
+    handles = [(C.c_void_p * 4)(*[C.c_void_p(e.cuda_event) for e in row[1:]]) for row in evs]
     t0 = time.perf_counter()
-    for _ in range(a.steps):
-        step(timer)
+    for s in range(a.steps):
+        evs[s][0].record()
+        nv.check(L.nvfp4_testing_set_launch_events(handles[s], 4))
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    nv.check(L.nvfp4_testing_set_launch_events(None, 0))
     ms_eager = (t1 - t0) * 1e3 / a.steps
-    parts = {"quantize": [], "gemm": [], "kv_append": [], "kv_dequant": []}
-    names = list(parts)
-    for s in range(a.steps):
-        for j, nm in enumerate(names):
-            parts[nm].append(timer.ev[5 * s + j].elapsed_time(timer.ev[5 * s + j + 1]) * 1e3)  # µs
-    us = {k: float(np.mean(v)) for k, v in parts.items()}
-    flops = 2.0 * M * N * K
-    q_bytes = M * K * 2.5625 + 4
-    kv_bytes = 2 * M * HD * 2.5625
-    gemm_tflops = flops / us["gemm"] / 1e6
-    q_gbs = q_bytes / us["quantize"] / 1e3
+    names = ["quantize_x", "gemm_up", "encode_h", "gemm_down"]
+    parts = {n: [evs[s][j].elapsed_time(evs[s][j + 1]) * 1e3 for s in range(a.steps)]
+             for j, n in enumerate(names)}
+    us = {n: float(np.mean(v)) for n, v in parts.items()}
 
-    # --- the headline: the same step captured once in a HIP graph, W replays
-    #     untimed, then exactly K replays timed (every call is replay-safe: the
-    #     quantiser's call counter lives in its workspace; the KV append writes
-    #     the same token range each replay, which the eager step gets from its
-    #     reset)
+    # the headline: the same step captured once in a HIP graph and replayed
     launch = "hip_graph"
     try:
         graph = torch.cuda.CUDAGraph()
@@ -273,49 +297,30 @@ def main():
     except Exception as exc:                     # capture unsupported: report the eager step
         log(f"graph capture failed ({exc}); reporting eager launches")
         launch, ms_per_step = "eager", ms_eager
+    flops_gemm = 2.0 * M * HID * D
+    flops = 2 * flops_gemm
     value = flops / (ms_per_step * 1e-3) / 1e12
 
-    # --- cold (MALL and L2 flushed) timings of the HBM-bound kernels
-    flush = CacheFlush(torch, dev)
-    cold = {"quantize": [], "kv_append": [], "kv_dequant": []}
-    for _ in range(10):
-        for nm in cold:
-            flush()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            if nm == "quantize":
-                e0.record(); nv.quantize_into(x, aq, asc, ag, qws); e1.record()
-            elif nm == "kv_append":
-                kv.reset()
-                e0.record(); kv.append(Kv, Vv); e1.record()
-            else:
-                e0.record(); kv.dequant(0, M, k_out, v_out); e1.record()
-            torch.cuda.synchronize()
-            cold[nm].append(e0.elapsed_time(e1) * 1e3)
-    del flush
-    cold_us = {k: float(np.median(v)) for k, v in cold.items()}
+    up_roof = roof_gemm(flops_gemm, us["gemm_up"])
+    up_roof.update({"kernel": "up GEMM + GELU-tanh epilogue + per-tile output maxima (k_gemm, 256x256 tiles)",
+                    "traffic": pmc_traffic(),
+                    "algorithmic_per_launch": f"2*M*N*K = {flops_gemm:.4e} flop (M=8192, N=14336, K=3072)",
+                    "avg_launch_us": round(us["gemm_up"], 2)})
+    h_bytes = M * HID * Q_BYTES_PER_ELEM                  # encode H: 2 B read + 0.5625 B written
+    x_bytes = M * D * Q_BYTES_PER_ELEM
+    kernels = {
+        "ffn_gemm_up": {"shape": [M, HID, D], "gelu": True, "us": pct(parts["gemm_up"]),
+                        "roofline": roof_gemm(flops_gemm, us["gemm_up"])},
+        "ffn_gemm_down": {"shape": [M, D, HID], "us": pct(parts["gemm_down"]),
+                          "roofline": roof_gemm(flops_gemm, us["gemm_down"])},
+        "ffn_quantize_x": {"shape": [M, D], "us": pct(parts["quantize_x"]),
+                           "roofline": roof_hbm(x_bytes, us["quantize_x"])},
+        "ffn_encode_h": {"shape": [M, HID], "us": pct(parts["encode_h"]),
+                         "roofline": roof_hbm(h_bytes, us["encode_h"])},
+    }
+    del graph
+    torch.cuda.empty_cache()
 
-    # --- back-to-back repetitions (one event pair around 50 calls): per-call
-    #     throughput without the event and launch gap of a single call
-    def batch_us(fn, reps=50):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-
-    def kv_once():
-        kv.reset()
-        kv.append(Kv, Vv)
-    batch = {"quantize": batch_us(lambda: nv.quantize_into(x, aq, asc, ag, qws)),
-             "kv_append": batch_us(kv_once),
-             "kv_dequant": batch_us(lambda: kv.dequant(0, M, k_out, v_out))}
-
-    traffic = pmc_traffic()
-    bm, bn = nv.gemm_tile(M, N, K)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -330,198 +335,120 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 operands, f16 MFMA, f32 accumulate",
+        "dtype": "nvfp4 operands (E2M1 + E4M3/16 + fp32), fp16 MFMA on exactly decoded products, fp32 accumulate",
         "data": "synthetic (seeded numpy draws, bf16)",
-        "config": {"workload": "DiT QKV projection: X[4096,3072] (0.1% x50 outliers) x W[9216,3072]^T "
-                               "+ bias, NVFP4 W4A4, then K/V (24x128) NVFP4 KV append + dequant",
-                   "M": M, "N": N, "K": K, "kv_heads": 24, "head_dim": 128, "gemm_tile": [bm, bn]},
-        "roofline": {"bound": "mfma", "kernel": "nvfp4 gemm (k_gemm)",
-                     "achieved": round(gemm_tflops, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
-                     "traffic": traffic,
-                     "algorithmic_per_launch": f"2*M*N*K = {flops:.4e} flop",
-                     "avg_launch_us": round(us["gemm"], 2)},
+        "config": {"workload": "DiT FFN pair: X[8192,3072] (0.1% x50 outliers) -> NVFP4 W4A4 up-projection "
+                               "to 14336 with GELU-tanh, H handed on in NVFP4 -> W4A4 down-projection to 3072",
+                   "M": M, "D": D, "hidden": HID,
+                   "gemm_tiles": {"up": list(nv.gemm_tile(M, HID, D)), "down": list(nv.gemm_tile(M, D, HID))}},
+        "roofline": up_roof,
         "breakdown_us": {k: round(v, 2) for k, v in us.items()},
-        "gemm": {"tflops": round(gemm_tflops, 1), "frac_f16_peak": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
-                 "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-                 "frac_fp4_peak": round(gemm_tflops / PEAK_FP4_TFLOPS, 4)},
-        # gbs_step: events around the call inside the timed steps; gbs_cold: one
-        # call after a 1 GiB cache flush (both include one launch gap);
-        # gbs_batch: 50 back-to-back calls, inputs warm in the MALL
-        "quantize": {"gbs_step": round(q_gbs, 1), "frac_hbm_step": round(q_gbs / PEAK_HBM_GBS, 4),
-                     "gbs_cold": round(q_bytes / cold_us["quantize"] / 1e3, 1),
-                     "frac_hbm_cold": round(q_bytes / cold_us["quantize"] / 1e3 / PEAK_HBM_GBS, 4),
-                     "gbs_batch": round(q_bytes / batch["quantize"] / 1e3, 1),
-                     "frac_hbm_batch": round(q_bytes / batch["quantize"] / 1e3 / PEAK_HBM_GBS, 4),
-                     "bytes_per_call": q_bytes},
-        "kv_append": {"gbs_step": round(kv_bytes / us["kv_append"] / 1e3, 1),
-                      "gbs_cold": round(kv_bytes / cold_us["kv_append"] / 1e3, 1),
-                      "frac_hbm_cold": round(kv_bytes / cold_us["kv_append"] / 1e3 / PEAK_HBM_GBS, 4),
-                      "gbs_batch": round(kv_bytes / batch["kv_append"] / 1e3, 1),
-                      "frac_hbm_batch": round(kv_bytes / batch["kv_append"] / 1e3 / PEAK_HBM_GBS, 4)},
-        "kv_dequant": {"gbs_step": round(kv_bytes / us["kv_dequant"] / 1e3, 1),
-                       "gbs_cold": round(kv_bytes / cold_us["kv_dequant"] / 1e3, 1),
-                       "frac_hbm_cold": round(kv_bytes / cold_us["kv_dequant"] / 1e3 / PEAK_HBM_GBS, 4),
-                       "gbs_batch": round(kv_bytes / batch["kv_dequant"] / 1e3, 1),
-                       "frac_hbm_batch": round(kv_bytes / batch["kv_dequant"] / 1e3 / PEAK_HBM_GBS, 4)},
-        "inputs_sha256": {"x": workloads.sha256(w.x)[:16], "w": workloads.sha256(w.w)[:16],
-                          "bias": workloads.sha256(w.bias)[:16]},
+        "kernels": kernels,
+        "inputs_sha256": {"x": workloads.sha256(w.x)[:16], "w_up": workloads.sha256(w.w)[:16],
+                          "w_down": workloads.sha256(w.w2)[:16]},
     }
 
-    if a.extended:
-        extended(a.extended, nv, torch, np, workloads, dev, up)
+    if not a.no_extras:
+        flush = CacheFlush(torch, dev)
+        copy_gbs = extras(kernels, nv, torch, np, workloads, dev, up, flush, x, lq_ws, qu)
+        out["copy_gbs"] = copy_gbs
+        for k in kernels.values():
+            r = k.get("roofline", {})
+            if r.get("bound") == "hbm" and "frac_of_copy" not in r:
+                r["frac_of_copy"] = round(r["achieved"] / copy_gbs, 4)
+        del flush
+    del x, hq, hs, hg, Y, lq_ws
+    torch.cuda.empty_cache()
 
     if not a.no_cpu_baseline:
         import oracle
         log("CPU oracle baseline")
-        qw_oracle = oracle.quantize(w.w)                # offline, outside the timed sample
-        out["cpu_baseline"] = cpu_baseline(w, qw_oracle, a.cpu_seconds)
+        qu_o, qd_o = oracle.quantize(w.w), oracle.quantize(w.w2)      # offline, outside the timed sample
+        out["cpu_baseline"] = cpu_baseline(w, qu_o, qd_o, a.cpu_seconds)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
 
 
-class CacheFlush:
-    """Evicts L2 and the MALL by reading a 1 GiB buffer (written once here).
+def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
+    """Per-kernel timings of the other configurations (added to `kernels`);
+    returns the measured 1 GiB device-copy rate in GB/s (read + write bytes)."""
+    # 1 GiB device copy: the practical HBM rate
+    log("extras: 1 GiB copy")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(3)
+    dst = torch.empty_like(src)
+    tc = time_us(torch, lambda: dst.copy_(src), 30, 5)
+    copy_gbs = 2 * (1 << 30) / np.percentile(tc, 50) / 1e3
+    kernels["copy_1gib"] = {"us": pct(tc), "gbs": round(copy_gbs, 1), "frac_hbm_peak": round(copy_gbs / PEAK_HBM_GBS, 4)}
+    del src, dst
 
-    A read leaves only clean lines behind.  Writing the buffer instead would
-    leave 1 GiB of dirty lines whose write-back then competes with the timed
-    kernel's reads (the long-context X quantiser took 113 us after a write
-    flush, 76 us after a read flush)."""
+    # FFN: the hidden activation H quantised by itself (cold), and the X quantiser cold
+    log("extras: FFN quantisers (cold)")
+    M, D = x_ffn.shape
+    H = nv.linear(x_ffn, *qu, gelu=True)
+    HID = H.shape[1]
+    hws = nv.workspace(nv.quantize_workspace_bytes(M, HID), dev)
+    hq = torch.empty((M, HID // 2), dtype=torch.uint8, device=dev)
+    hs = torch.empty((M, HID // 16), dtype=torch.uint8, device=dev)
+    hg = torch.empty((1,), dtype=torch.float32, device=dev)
+    t = time_us(torch, lambda: nv.quantize_into(H, hq, hs, hg, hws), 100, 5, flush)
+    kernels["ffn_quantize_h_cold"] = {"shape": [M, HID], "us": pct(t),
+                                      "roofline": roof_hbm(M * HID * Q_BYTES_PER_ELEM + 4, float(np.median(t)))}
+    xq = torch.empty((M, D // 2), dtype=torch.uint8, device=dev)
+    xs = torch.empty((M, D // 16), dtype=torch.uint8, device=dev)
+    xws = nv.workspace(nv.quantize_workspace_bytes(M, D), dev)
+    t = time_us(torch, lambda: nv.quantize_into(x_ffn, xq, xs, hg, xws), 100, 5, flush)
+    kernels["ffn_quantize_x_cold"] = {"shape": [M, D], "us": pct(t),
+                                      "roofline": roof_hbm(M * D * Q_BYTES_PER_ELEM + 4, float(np.median(t)))}
+    del H, hq, hs, hws, xq, xs, xws
+    torch.cuda.empty_cache()
 
-    def __init__(self, torch, dev):
-        self.buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(7).view(torch.int64)
-        torch.cuda.synchronize()
-
-    def __call__(self):
-        self.buf.max()
-
-
-def _time_events(torch, fn, reps, flush=None):
-    ts = []
-    for _ in range(reps):
-        if flush is not None:
-            flush()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e3)
-    return ts
-
-
-def _dequant_rel_err(torch, x, codes, scales, g):
-    """‖x − Dequant(q)‖ / ‖x‖ in fp32 (a reported statistic, computed with torch)."""
-    e2m1 = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6],
-                        dtype=torch.float32, device=x.device)
-    lo, hi = (codes & 15).long(), (codes >> 4).long()
-    vals = torch.stack((e2m1[lo], e2m1[hi]), dim=-1).reshape(codes.shape[0], -1)
-    s = scales.view(torch.float8_e4m3fn).float().repeat_interleave(16, dim=1)
-    d = vals * s * g.float()
-    xf = x.float()
-    return float(torch.linalg.vector_norm(xf - d) / torch.linalg.vector_norm(xf))
-
-
-def extended(path, nv, torch, np, workloads, dev, up):
-    """Per-kernel numbers on the other DiT shapes and the full KV sequence."""
-    lines = []
-    flush = CacheFlush(torch, dev)
-    shapes = [("qkv", workloads.qkv, False), ("ffn_up", workloads.ffn, True), ("long", workloads.long_ctx, False)]
-    for name, fn, gelu in shapes:
-        log(f"extended: {name}")
-        w = fn()
-        x, W = up(w.x), up(w.w)
-        M, K, N = w.M, w.K, w.N
-        wq, wsc, wg = nv.quantize(W)
-        aq, asc, ag = nv.quantize(x)
-        bias = up(w.bias) if w.bias is not None else None
-        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        g = lambda: nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, gelu=gelu, out=C)
-        g(); torch.cuda.synchronize()
-        tg = float(np.median(_time_events(torch, g, 20)))
-        qws = nv.workspace(nv.quantize_workspace_bytes(M, K), dev)
-        q = lambda: nv.quantize_into(x, aq, asc, ag, qws)
-        tq = float(np.median(_time_events(torch, q, 20, flush)))
-        qb = M * K * 2.5625
-        lines.append({"shape": name, "M": M, "N": N, "K": K, "gemm_us": tg,
-                      "gemm_tflops": 2 * M * N * K / tg / 1e6, "tile": nv.gemm_tile(M, N, K),
-                      "quantize_us_cold": tq, "quantize_gbs_cold": qb / tq / 1e3})
+    # QKV projection and the long-context out-projection: GEMM (warm, back to
+    # back) and the activation quantiser (cold); QKV's K/V column slices into
+    # a KV cache and back (cold)
+    for name, fn in (("qkv", workloads.qkv), ("long", workloads.long_ctx)):
+        log(f"extras: {name}")
+        wl = fn()
+        Mx, K = wl.x.shape
+        N = wl.w.shape[0]
+        xd = up(wl.x)
+        wq = nv.quantize(up(wl.w))
+        bias = up(wl.bias) if wl.bias is not None else None
+        aq, asc, ag = nv.quantize(xd)
+        Cm = torch.empty((Mx, N), dtype=torch.bfloat16, device=dev)
+        t = time_us(torch, lambda: nv.gemm(aq, asc, ag, *wq, bias=bias, out=Cm), 30, 10)
+        kernels[f"{name}_gemm"] = {"shape": [Mx, N, K], "bias": bias is not None, "tile": list(nv.gemm_tile(Mx, N, K)),
+                                   "us": pct(t), "roofline": roof_gemm(2.0 * Mx * N * K, float(np.median(t)))}
+        qws = nv.workspace(nv.quantize_workspace_bytes(Mx, K), dev)
+        t = time_us(torch, lambda: nv.quantize_into(xd, aq, asc, ag, qws), 100, 5, flush)
+        kernels[f"{name}_quantize_x_cold"] = {"shape": [Mx, K], "us": pct(t),
+                                              "roofline": roof_hbm(Mx * K * Q_BYTES_PER_ELEM + 4, float(np.median(t)))}
         if name == "qkv":
-            # adaptive {4, 6} block scales: time (cold) and normwise dequant error
-            # against the standard amax→6 encoding, for X and for the weights
-            for tname, t, rows in (("X", x, M), ("W", W, N)):
-                ws_t = nv.workspace(nv.quantize_workspace_bytes(rows, K), dev)
-                oc = torch.empty((rows, K // 2), dtype=torch.uint8, device=dev)
-                os_ = torch.empty((rows, K // 16), dtype=torch.uint8, device=dev)
-                og = torch.empty((1,), dtype=torch.float32, device=dev)
-                rec = {"shape": f"qkv_{tname}_adaptive46", "rows": rows, "K": K}
-                for mode, ad in (("std", False), ("adaptive", True)):
-                    f = lambda: nv.quantize_into(t, oc, os_, og, ws_t, adaptive46=ad)
-                    tt = float(np.median(_time_events(torch, f, 10, flush)))
-                    f(); torch.cuda.synchronize()
-                    rec[f"{mode}_us_cold"] = tt
-                    rec[f"{mode}_gbs_cold"] = rows * K * 2.5625 / tt / 1e3
-                    rec[f"{mode}_rel_err"] = _dequant_rel_err(torch, t, oc, os_, og)
-                lines.append(rec)
-            # two-dimensional 16x16 weight blocks (offline weight quantisation):
-            # time (cold) and normwise dequant error against the 1-D blocks
-            ws_w = nv.workspace(nv.quantize_workspace_bytes(N, K), dev)
-            oc = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-            os_ = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
-            og = torch.empty((1,), dtype=torch.float32, device=dev)
-            rec = {"shape": "qkv_W_blocks2d", "rows": N, "K": K}
-            for mode, b2 in (("1d", False), ("2d", True)):
-                f = lambda: nv.quantize_into(W, oc, os_, og, ws_w, blocks2d=b2)
-                tt = float(np.median(_time_events(torch, f, 10, flush)))
-                f(); torch.cuda.synchronize()
-                rec[f"{mode}_us_cold"] = tt
-                rec[f"{mode}_gbs_cold"] = N * K * 2.5625 / tt / 1e3
-                rec[f"{mode}_rel_err"] = _dequant_rel_err(torch, W, oc, os_, og)
-            lines.append(rec)
-        if name == "ffn_up":
-            # down projection: H = GELU output (bf16 [8192, 14336]) quantised, times W_down
-            Wd = up(w.w2)
-            dq, dsc, dg = nv.quantize(Wd)
-            hq, hsc, hg = nv.quantize(C)
-            Cd = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-            gd = lambda: nv.gemm(hq, hsc, hg, dq, dsc, dg, out=Cd)
-            gd(); torch.cuda.synchronize()
-            td = float(np.median(_time_events(torch, gd, 20)))
-            hws = nv.workspace(nv.quantize_workspace_bytes(M, N), dev)
-            qh = lambda: nv.quantize_into(C, hq, hsc, hg, hws)
-            tqh = float(np.median(_time_events(torch, qh, 20, flush)))
-            lines.append({"shape": "ffn_down", "M": M, "N": K, "K": N, "gemm_us": td,
-                          "gemm_tflops": 2 * M * N * K / td / 1e6, "tile": nv.gemm_tile(M, K, N),
-                          "quantize_us_cold": tqh, "quantize_gbs_cold": M * N * 2.5625 / tqh / 1e3})
-            # the whole FFN: linear(up, GELU) → quantise H → down GEMM, against
-            # linear_q (H's maxima from the up GEMM's epilogue, H read once)
-            lws = nv.workspace(nv.linear_workspace_bytes(M, K), dev)
-            qws_ = nv.workspace(nv.linear_q_workspace_bytes(M, N, K), dev)
+            kv = nv.KVCache(Mx, 24, 128, max_chunks=1, device=dev)
+            Kv, Vv = Cm[:, 3072:6144], Cm[:, 6144:9216]
+            ko = torch.empty((Mx, 24, 128), dtype=torch.bfloat16, device=dev)
+            vo = torch.empty_like(ko)
 
-            def chain():
-                nv.linear(x, wq, wsc, wg, gelu=True, out=C, ws=lws)
-                nv.quantize_into(C, hq, hsc, hg, hws)
-                nv.gemm(hq, hsc, hg, dq, dsc, dg, out=Cd)
-
-            def chain_q():
-                nv.linear_q(x, wq, wsc, wg, gelu=True, out=(hq, hsc, hg), ws=qws_)
-                nv.gemm(hq, hsc, hg, dq, dsc, dg, out=Cd)
-            chain(); chain_q(); torch.cuda.synchronize()
-            tc = float(np.median(_time_events(torch, chain, 10, flush)))
-            tcq = float(np.median(_time_events(torch, chain_q, 10, flush)))
-            flops_ffn = 4.0 * M * N * K
-            lines.append({"shape": "ffn_chain", "M": M, "D": K, "hidden": N,
-                          "linear_quantize_gemm_us": tc, "linear_q_gemm_us": tcq,
-                          "tflops_unfused": flops_ffn / tc / 1e6, "tflops_linear_q": flops_ffn / tcq / 1e6})
-            del qws_, lws
-        del x, W, C
+            def app():
+                kv.reset()
+                kv.append(Kv, Vv)
+            t = time_us(torch, app, 100, 5, flush)
+            kvb = 2 * Mx * 3072 * Q_BYTES_PER_ELEM + 8
+            kernels["qkv_kv_append_cold"] = {"tokens": Mx, "us": pct(t), "roofline": roof_hbm(kvb, float(np.median(t)))}
+            t = time_us(torch, lambda: kv.dequant(0, Mx, ko, vo), 100, 5, flush)
+            kernels["qkv_kv_dequant_cold"] = {"tokens": Mx, "us": pct(t),
+                                              "roofline": roof_hbm(2 * Mx * 3072 * Q_BYTES_PER_ELEM, float(np.median(t)))}
+            del kv, ko, vo
+        del xd, wq, aq, asc, Cm, qws, wl
         torch.cuda.empty_cache()
-    # the 65536-token KV sequence: 74 appends of 880 tokens + one of 416, then a full dequant
-    log("extended: kv sequence")
+
+    # the 65536-token KV cache: 74 appends of 880 tokens + one of 416, then a
+    # read-back of the whole cache
+    log("extras: 65536-token KV sequence")
     Kb, Vb, sizes = workloads.kv()
     kd, vd = up(Kb), up(Vb)
     T = Kb.shape[0]
+    del Kb, Vb
     cache = nv.KVCache(T, 24, 128, max_chunks=len(sizes), device=dev)
     starts = np.r_[0, np.cumsum(sizes)]
 
@@ -529,39 +456,51 @@ def extended(path, nv, torch, np, workloads, dev, up):
         cache.reset()
         for i in range(len(sizes)):
             cache.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]])
-
-    seq(); torch.cuda.synchronize()
-    tseq = float(np.median(_time_events(torch, seq, 5, flush)))
-
-    def seq46():
+    t = time_us(torch, seq, 10, 2, flush)
+    kvb = 2 * T * 3072 * Q_BYTES_PER_ELEM + 8 * len(sizes)
+    kernels["kv65536_append_sequence_cold"] = {"appends": len(sizes), "tokens": T, "us": pct(t),
+                                               "roofline": roof_hbm(kvb, float(np.median(t)))}
+    # each 880-token append inside the back-to-back sequence: an event after
+    # every append, per-append time = the gap between consecutive events
+    per = []
+    for _ in range(4):
+        flush()
         cache.reset()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
+        ev[0].record()
         for i in range(len(sizes)):
-            cache.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]], adaptive46=True)
-
-    seq46(); torch.cuda.synchronize()
-    tseq46 = float(np.median(_time_events(torch, seq46, 5, flush)))
-    # the same 75 appends captured once in a HIP graph (each replay writes the
-    # token ranges and chunk slots fixed at capture time)
-    seq_graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(seq_graph):
-        seq()
-    seq_graph.replay(); torch.cuda.synchronize()
-    tseq_graph = float(np.median(_time_events(torch, seq_graph.replay, 5, flush)))
-    seq(); torch.cuda.synchronize()
+            cache.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]])
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        per += [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(1, len(sizes) - 1)]
+    b880 = 2 * 880 * 3072 * Q_BYTES_PER_ELEM + 8
+    kernels["kv880_append"] = {"tokens": 880, "us": pct(per), "roofline": roof_hbm(b880, float(np.median(per)))}
     ko = torch.empty((T, 24, 128), dtype=torch.bfloat16, device=dev)
     vo = torch.empty_like(ko)
-    deq = lambda: cache.dequant(0, T, ko, vo)
-    tdq = float(np.median(_time_events(torch, deq, 10, flush)))
-    kvb = 2 * T * 3072 * 2.5625
-    lines.append({"shape": "kv_65536", "appends": len(sizes), "append_seq_us": tseq,
-                  "append_seq_gbs": kvb / tseq / 1e3, "append_us_per_chunk": tseq / len(sizes),
-                  "append_seq_adaptive46_us": tseq46, "append_seq_graph_us": tseq_graph,
-                  "append_seq_graph_gbs": kvb / tseq_graph / 1e3,
-                  "dequant_us": tdq, "dequant_gbs": kvb / tdq / 1e3})
-    with open(path, "w") as f:
-        for l in lines:
-            f.write(json.dumps(l) + "\n")
-    log(f"extended results written to {path}")
+    t = time_us(torch, lambda: cache.dequant(0, T, ko, vo), 100, 5, flush)
+    kernels["kv65536_dequant_cold"] = {"tokens": T, "us": pct(t),
+                                       "roofline": roof_hbm(2 * T * 3072 * Q_BYTES_PER_ELEM, float(np.median(t)))}
+    del kd, vd, cache, ko, vo
+    torch.cuda.empty_cache()
+    return round(float(copy_gbs), 1)
+
+
+def gemm_clock(a, nv, torch, np, workloads, dev, up):
+    """The QKV GEMM launched 20 times on the benchmark's operands, then 20 times
+    after filling the codes and scales with constant bytes."""
+    w = workloads.qkv()
+    M, K, N = w.M, w.K, w.N
+    x, bias = up(w.x), up(w.bias)
+    wq, wsc, wg = nv.quantize(up(w.w))
+    aq, asc, ag = nv.quantize(x)
+    Cm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for kind in ("benchmark", "constant"):
+        if kind == "constant":              # fixed byte patterns, every element alike
+            aq.fill_(0x35); wq.fill_(0x53); asc.fill_(0x38); wsc.fill_(0x30)
+        t = time_us(torch, lambda: nv.gemm(aq, asc, ag, wq, wsc, wg, bias=bias, out=Cm), 20, 3)
+        res[kind + "_us"] = float(np.mean(t))
+    print(json.dumps({"gemm_clock": res, "launches_per_kind": 20, "warmup_per_kind": 3}))
 
 
 if __name__ == "__main__":

@@ -63,6 +63,7 @@ _SIGS = {
                            C.c_int),
     "nvfp4_kv_dequant": ([C.POINTER(KVCacheDesc), _i64, _i64, _p, _p, _p], C.c_int),
     "nvfp4_testing_set_quantize_wait": ([C.c_uint64], C.c_uint64),
+    "nvfp4_testing_set_launch_events": ([C.POINTER(C.c_void_p), C.c_int], C.c_int),
     "nvfp4_strerror": ([C.c_int], C.c_char_p),
     "nvfp4_last_error": ([], C.c_char_p),
 }

@@ -55,6 +55,24 @@ int hip_status(hipError_t e, const char *who) {
   return fail(NVFP4_EHIP, std::string(who) + ": " + hipGetErrorString(e));
 }
 
+// Testing hook state (nvfp4_testing_set_launch_events): events still to be
+// recorded, one after each launch step, on the step's stream.
+std::atomic<void *const *> g_events{nullptr};
+std::atomic<int> g_events_left{0}, g_events_next{0};
+
+// Status of a launch step on `st`; after a successful one, records the next
+// pending testing event there (if any).
+int launched(hipError_t e, hipStream_t st, const char *who) {
+  const int s = hip_status(e, who);
+  if (s == NVFP4_OK && g_events_left.load(std::memory_order_relaxed) > 0) {
+    void *const *ev = g_events.load(std::memory_order_relaxed);
+    const int i = g_events_next.fetch_add(1, std::memory_order_relaxed);
+    g_events_left.fetch_sub(1, std::memory_order_relaxed);
+    if (ev != nullptr) return hip_status(hipEventRecord(static_cast<hipEvent_t>(ev[i]), st), who);
+  }
+  return s;
+}
+
 // nvfp4_linear workspace: [codes | scales | gscale | amax partials]
 struct LinearWs {
   size_t codes, scales, gscale, partials, total;
@@ -121,10 +139,10 @@ int nvfp4_quantize_ex(const uint16_t *x, int64_t M, int64_t K, uint32_t qflags, 
   if (ws == nullptr || ws_bytes < kQuantWs) return fail(NVFP4_EWORKSPACE, "quantize: workspace too small");
   if ((s = check_ptr(ws, "ws"))) return s;
   nvfp4::QuantJob j{x, codes, scales, gscale, ws, M, K, K};
-  return hip_status(nvfp4::launch_quantize(&j, 1, static_cast<hipStream_t>(stream), nullptr,
-                                           (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0,
-                                           (qflags & NVFP4_Q_BLOCK_2D) != 0),
-                    "quantize");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(nvfp4::launch_quantize(&j, 1, st, nullptr, (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0,
+                                         (qflags & NVFP4_Q_BLOCK_2D) != 0),
+                  st, "quantize");
 }
 
 int nvfp4_quantize(const uint16_t *x, int64_t M, int64_t K, uint8_t *codes, uint8_t *scales,
@@ -138,7 +156,8 @@ int nvfp4_gemm(const uint8_t *Aq, const uint8_t *As, const float *Ag, const uint
   int s = check_gemm_args(Aq, As, Ag, Wq, Ws, Wg, bias, C, M, N, K, flags, true);
   if (s) return s;
   nvfp4::GemmArgs a{Aq, As, Ag, Wq, Ws, Wg, bias, C, M, N, K, flags};
-  return hip_status(nvfp4::launch_gemm(a, static_cast<hipStream_t>(stream)), "gemm");
+  return launched(nvfp4::launch_gemm(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
+                  "gemm");
 }
 
 int nvfp4_gemm_tile(int64_t M, int64_t N, int64_t K, int *bm, int *bn) {
@@ -171,9 +190,9 @@ int nvfp4_linear(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, const 
   float *ag = reinterpret_cast<float *>(base + w.gscale);
   hipStream_t st = static_cast<hipStream_t>(stream);
   nvfp4::QuantJob j{x, aq, as, ag, base + w.partials, M, K, K};
-  if ((s = hip_status(nvfp4::launch_quantize(&j, 1, st), "linear/quantize"))) return s;
+  if ((s = launched(nvfp4::launch_quantize(&j, 1, st), st, "linear/quantize"))) return s;
   nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, C, M, N, K, flags};
-  return hip_status(nvfp4::launch_gemm(a, st), "linear/gemm");
+  return launched(nvfp4::launch_gemm(a, st), st, "linear/gemm");
 }
 
 // ---------------------------------------------------------------------------
@@ -252,9 +271,9 @@ int nvfp4_linear_noalloc(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws
   float *ag = reinterpret_cast<float *>(base + kNoAllocGscale);
   hipStream_t st = static_cast<hipStream_t>(stream);
   nvfp4::QuantJob j{x, aq, as, ag, base + kNoAllocQuant, M, K, K};
-  if ((s = hip_status(nvfp4::launch_quantize(&j, 1, st), "linear_noalloc/quantize"))) return s;
+  if ((s = launched(nvfp4::launch_quantize(&j, 1, st), st, "linear_noalloc/quantize"))) return s;
   nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, C, M, N, K, flags};
-  return hip_status(nvfp4::launch_gemm(a, st), "linear_noalloc/gemm");
+  return launched(nvfp4::launch_gemm(a, st), st, "linear_noalloc/gemm");
 }
 
 int nvfp4_linear_q_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes) {
@@ -290,14 +309,14 @@ int nvfp4_linear_q(const uint16_t *x, const uint8_t *Wq, const uint8_t *Ws, cons
   uint32_t *slots = reinterpret_cast<uint32_t *>(base + w.slots);
   hipStream_t st = static_cast<hipStream_t>(stream);
   nvfp4::QuantJob jx{x, aq, as, ag, base + w.lin.partials, M, K, K};
-  if ((s = hip_status(nvfp4::launch_quantize(&jx, 1, st), "linear_q/quantize"))) return s;
+  if ((s = launched(nvfp4::launch_quantize(&jx, 1, st), st, "linear_q/quantize"))) return s;
   nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, H, M, N, K, flags};
   a.tile_amax = slots;
   const int64_t tiles = nvfp4::gemm_tile_count(a);
   if (tiles > w.max_tiles) return fail(NVFP4_EHIP, "linear_q: internal tile count exceeds the workspace");
-  if ((s = hip_status(nvfp4::launch_gemm(a, st), "linear_q/gemm"))) return s;
+  if ((s = launched(nvfp4::launch_gemm(a, st), st, "linear_q/gemm"))) return s;
   nvfp4::QuantJob jh{H, Hq, Hs, Hg, nullptr, M, N, N};
-  return hip_status(nvfp4::launch_encode_from_partials(jh, slots, tiles, st), "linear_q/encode");
+  return launched(nvfp4::launch_encode_from_partials(jh, slots, tiles, st), st, "linear_q/encode");
 }
 
 int nvfp4_kv_init(nvfp4_kv_cache *c) {
@@ -356,9 +375,9 @@ int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, 
       {V, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
        parts + kQuantWs, T, e, ld}};
   nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
-  s = hip_status(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark,
-                                        (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0),
-                 "kv_append");
+  s = launched(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark,
+                                      (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0),
+               static_cast<hipStream_t>(stream), "kv_append");
   if (s) return s;
   c->n_tokens += T;
   c->n_chunks += 1;
@@ -391,10 +410,21 @@ int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1, uint16_t *
   a.t0 = t0;
   a.t1 = t1;
   a.elems_per_token = c->heads * c->head_dim;
-  return hip_status(nvfp4::launch_kv_dequant(a, static_cast<hipStream_t>(stream)), "kv_dequant");
+  return launched(nvfp4::launch_kv_dequant(a, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "kv_dequant");
 }
 
 uint64_t nvfp4_testing_set_quantize_wait(uint64_t ticks) { return nvfp4::set_resident_wait_ticks(ticks); }
+
+int nvfp4_testing_set_launch_events(void *const *events, int count) {
+  if (count < 0 || (count > 0 && events == nullptr))
+    return fail(NVFP4_EINVAL, "testing_set_launch_events: bad event list");
+  g_events_left.store(0, std::memory_order_relaxed);
+  g_events.store(events, std::memory_order_relaxed);
+  g_events_next.store(0, std::memory_order_relaxed);
+  g_events_left.store(count, std::memory_order_relaxed);
+  return NVFP4_OK;
+}
 
 const char *nvfp4_strerror(int status) {
   switch (status) {

@@ -219,3 +219,9 @@ def test_linear_noalloc_rejects(L):
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, lim // 3072 + 1, 64, 3072, 0, None) == EINVAL
     msg = L.nvfp4_last_error()
     assert b"NVFP4_NOALLOC_MAX_ELEMENTS" in msg and str(lim).encode() in msg
+
+
+def test_launch_event_hook_rejects(L):
+    assert L.nvfp4_testing_set_launch_events(None, 2) == EINVAL
+    assert L.nvfp4_testing_set_launch_events(None, -1) == EINVAL
+    assert L.nvfp4_testing_set_launch_events(None, 0) == 0
