@@ -4,26 +4,46 @@
 // KV cache is stored quantised per chunk and read back through a dequant
 // kernel; 二、方法 / NVFP4 量化格式: Dequant = X^FP4 · α^FP8 · α^FP32.
 //
-// Layout of the work: every lane turns one 8-element chunk (4 code bytes, one
+// Layout of the work: every lane turns one 8-element group (4 code bytes, one
 // scale byte shared with its neighbour lane) into 16 bytes of bf16, so each
-// load and store instruction of a wave covers consecutive memory; a workgroup
-// handles kKvU chunks per lane.  out = bf16(fl32(fl32(E2M1·S)·g)), where g is
-// the tensor scale of the append that wrote the token, found by binary search
-// over the chunk start offsets (copied to LDS when they fit).  The E2M1·S
-// product is exact in binary32.
+// load and store instruction of a wave covers consecutive memory; a thread
+// handles kKvU groups, kKvThreads apart.  out = bf16(fl32(fl32(E2M1·S)·g)),
+// where g is the tensor scale of the append that wrote the token (the E2M1·S
+// product is exact in binary32).
+//
+// Finding each token's append: a wave covers few tokens (under 3 for 24
+// heads of 128), so it first brackets its token range: the appends holding
+// its first and its last token, each found by a 64-wide search (every lane
+// compares one chunk start, a ballot counts the starts at or below the token;
+// one round per 64 appends).  Then each lane searches only inside that
+// bracket, which is usually a single append.  The starts are read from global
+// memory (they stay in the caches); no LDS, no barrier.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nvfp4 {
 
 constexpr int kKvThreads = 256;
-constexpr int kKvU = 4;                    // chunks per lane
-constexpr int kKvLdsStarts = 2048;         // chunk starts held in LDS
+constexpr int kKvU = 4;                    // 8-element groups per thread
 
-// Index of the chunk holding token t: starts[lo] <= t < starts[lo + 1].
-template <typename P>
-__device__ __forceinline__ int64_t chunk_of(P starts, int64_t n_chunks, int64_t t) {
-  int64_t lo = 0, hi = n_chunks - 1;
+// Index of the append holding token t (starts[c] <= t < starts[c + 1]),
+// computed by the whole wave for a wave-uniform t: the number of starts
+// starts[1..n_chunks-1] that are <= t.
+__device__ __forceinline__ int64_t chunk_of_uniform(const int64_t *starts, int64_t n_chunks, int64_t t) {
+  const int lane = threadIdx.x & 63;
+  int64_t c = 0;
+  for (int64_t base = 1; base < n_chunks; base += 64) {
+    const int64_t j = base + lane;
+    const bool le = j < n_chunks && starts[j] <= t;
+    const int n = __builtin_popcountll(__ballot(le));
+    c += n;
+    if (n < 64) break;                       // starts are increasing: no later one is <= t
+  }
+  return c;
+}
+
+// Index of the append holding token t, knowing it lies in [lo, hi].
+__device__ __forceinline__ int64_t chunk_in(const int64_t *starts, int64_t lo, int64_t hi, int64_t t) {
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) >> 1;
     if (starts[mid] <= t) lo = mid; else hi = mid - 1;
@@ -51,45 +71,48 @@ __device__ __forceinline__ u32x4 dequant_dword(uint32_t w, float s, float g) {
 __global__ void __launch_bounds__(kKvThreads) k_kv_dequant(KvDequantArgs a) {
   const int which = blockIdx.y;
   const int64_t e = a.elems_per_token;
-  const int64_t base = a.t0 * e / 8;                 // first chunk of the range
-  const int64_t chunks = (a.t1 - a.t0) * e / 8;
+  const int64_t base = a.t0 * e / 8;                 // first group of the range
+  const int64_t groups = (a.t1 - a.t0) * e / 8;
   const uint32_t *codes = reinterpret_cast<const uint32_t *>(a.codes[which]) + base;
   const uint8_t *scales = a.scales[which] + base / 2;
   u32x4 *out = reinterpret_cast<u32x4 *>(a.out[which]);
-  const bool narrow = 8 * (chunks + kKvThreads * kKvU) < (int64_t(1) << 32);   // 32-bit token division
+  const bool narrow = 8 * (groups + kKvThreads * kKvU) < (int64_t(1) << 32);   // 32-bit token division
 
-  // loads first, so the chunk search below overlaps them
+  // loads first, so the append search below overlaps them
   uint32_t c[kKvU], sb[kKvU];
+  int64_t q[kKvU];
 #pragma unroll
   for (int i = 0; i < kKvU; ++i) {
-    const int64_t q = ((int64_t)blockIdx.x * kKvU + i) * kKvThreads + threadIdx.x;
-    c[i] = q < chunks ? codes[q] : 0u;
-    sb[i] = q < chunks ? scales[q >> 1] : 0u;
+    q[i] = ((int64_t)blockIdx.x * kKvU + i) * kKvThreads + threadIdx.x;
+    c[i] = q[i] < groups ? codes[q[i]] : 0u;
+    sb[i] = q[i] < groups ? scales[q[i] >> 1] : 0u;
   }
-  __shared__ int64_t st[kKvLdsStarts];
-  const bool in_lds = a.n_chunks < kKvLdsStarts;
-  if (in_lds) {
-    for (int64_t j = threadIdx.x; j <= a.n_chunks; j += kKvThreads) st[j] = a.chunk_start[j];
-    __syncthreads();
-  }
+  auto token = [&](int64_t g) {
+    return a.t0 + (narrow ? (int64_t)((uint32_t)(8 * g) / (uint32_t)e) : (8 * g) / e);
+  };
+  // the wave's groups: q[0] of its lane 0 to q[kKvU-1] of its lane 63
+  const int64_t w0 = q[0] - (threadIdx.x & 63);
+  int64_t w1 = w0 + (int64_t)(kKvU - 1) * kKvThreads + 63;
+  if (w1 >= groups) w1 = groups - 1;
+  if (w0 >= groups) return;                           // the whole wave is past the range
+  const int64_t c_lo = chunk_of_uniform(a.chunk_start, a.n_chunks, token(w0));
+  const int64_t c_hi = chunk_of_uniform(a.chunk_start, a.n_chunks, token(w1));
 #pragma unroll
   for (int i = 0; i < kKvU; ++i) {
-    const int64_t q = ((int64_t)blockIdx.x * kKvU + i) * kKvThreads + threadIdx.x;
-    const int64_t t = a.t0 + (narrow ? (int64_t)((uint32_t)(8 * q) / (uint32_t)e) : (8 * q) / e);
-    const int64_t ci = in_lds ? chunk_of(st, a.n_chunks, t) : chunk_of(a.chunk_start, a.n_chunks, t);
+    if (q[i] >= groups) continue;
+    const int64_t ci = c_lo == c_hi ? c_lo : chunk_in(a.chunk_start, c_lo, c_hi, token(q[i]));
     const float g = a.gscale[2 * ci + which];
     const u32x4 o = dequant_dword(c[i], e4m3_decode(sb[i]), g);
-    // non-temporal: the output streams past L2 and the MALL (measured 5.9 →
-    // 7.2 TB/s on a 65536-token read-back)
-    if (q < chunks) __builtin_nontemporal_store(o, &out[q]);
+    // non-temporal: the output streams past L2 and the MALL
+    __builtin_nontemporal_store(o, &out[q[i]]);
   }
 }
 
 hipError_t launch_kv_dequant(const KvDequantArgs &a, hipStream_t stream) {
-  const int64_t chunks = (a.t1 - a.t0) * (a.elems_per_token / 8);
-  if (chunks <= 0) return hipSuccess;
+  const int64_t groups = (a.t1 - a.t0) * (a.elems_per_token / 8);
+  if (groups <= 0) return hipSuccess;
   const int64_t per_block = (int64_t)kKvThreads * kKvU;
-  const int64_t blocks = (chunks + per_block - 1) / per_block;
+  const int64_t blocks = (groups + per_block - 1) / per_block;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_kv_dequant, dim3((unsigned)blocks, 2), dim3(kKvThreads), 0, stream, a);
   return hipGetLastError();
