@@ -96,16 +96,19 @@ __device__ __forceinline__ float gelu_tanh(float y) {
 }
 
 constexpr int kChunks = kBK / 32;        // 16-byte code chunks per row per stage
-constexpr int kPadRows = 4;              // LDS row padding per chunk column
+constexpr int kPadRows = 2;              // LDS row padding per chunk column
+// rows of each operand's scale-pair region: one per thread, so every thread
+// stores its own row (the rows past the tile's are never read)
+constexpr int kScaleRows = kGemmThreads;
 
 template <int WM, int WN>
 struct Tile {
   static constexpr int BM = 64 * WM, BN = 64 * WN;
   static constexpr int A_CODE = 0;
   static constexpr int W_CODE = A_CODE + kChunks * (BM + kPadRows) * 16;
-  static constexpr int A_SCALE = W_CODE + kChunks * (BN + kPadRows) * 16;   // [2][BM][4 pairs]
-  static constexpr int W_SCALE = A_SCALE + BM * 32;
-  static constexpr int STAGE = W_SCALE + BN * 32;
+  static constexpr int A_SCALE = W_CODE + kChunks * (BN + kPadRows) * 16;   // [2][256][4 pairs]
+  static constexpr int W_SCALE = A_SCALE + kScaleRows * 32;
+  static constexpr int STAGE = W_SCALE + kScaleRows * 32;
   static constexpr int GG = 2 * STAGE;      // fl32(Ag·Wg)
   static constexpr int BIAS = GG + 16;      // [BN] bf16 bias of the tile's columns
   static constexpr int LDS = BIAS + BN * 2;
@@ -162,7 +165,7 @@ __device__ __forceinline__ void fill_load(Fill<ROWS> &f, const Operand &op, int6
 
 // Codes go to LDS as they are; the 8 scale bytes of a row are expanded to
 // fp16 scale pairs (scale_pair_f16) and stored as two 16-byte groups, blocks
-// {0, 1, 4, 5} in the first ROWS·16 bytes and {2, 3, 6, 7} in the next: group
+// {0, 1, 4, 5} in the first kScaleRows·16 bytes and {2, 3, 6, 7} in the next: group
 // h holds the blocks 2h, 2h+1, 4+2h, 5+2h that a lane with that h decodes, and
 // a wave's accesses to one group are contiguous.
 template <int ROWS>
@@ -174,13 +177,14 @@ __device__ __forceinline__ void fill_store(const Fill<ROWS> &f, uint8_t *code_ld
     const int row = q >> 2, c = q & 3;
     *reinterpret_cast<u32x4 *>(code_lds + (c * (ROWS + kPadRows) + row) * 16) = f.code[it];
   }
-  const int srow = t < ROWS ? t : ROWS - 1;
+  // every thread stores its own row (threads past the tile's rows store a
+  // copy of the last row that nothing reads), so no two lanes share an address
   const uint32_t lo = f.scale.x, hi = f.scale.y;     // blocks 0..3, 4..7
   const u32x4 g0 = {scale_pair_f16(lo), scale_pair_f16(lo >> 8), scale_pair_f16(hi), scale_pair_f16(hi >> 8)};
   const u32x4 g1 = {scale_pair_f16(lo >> 16), scale_pair_f16(lo >> 24), scale_pair_f16(hi >> 16),
                     scale_pair_f16(hi >> 24)};
-  *reinterpret_cast<u32x4 *>(scale_lds + srow * 16) = g0;
-  *reinterpret_cast<u32x4 *>(scale_lds + (ROWS + srow) * 16) = g1;
+  *reinterpret_cast<u32x4 *>(scale_lds + t * 16) = g0;
+  *reinterpret_cast<u32x4 *>(scale_lds + (kScaleRows + t) * 16) = g1;
 }
 
 // A wave's view of one stage: codes of both sub-steps and the lane's four
@@ -198,7 +202,7 @@ __device__ __forceinline__ void frag_read(Frag<WM + WN> &fr, const uint8_t *buf,
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
     const int row = wm * 32 * WM + 32 * i + r;
-    fr.sc[i] = *reinterpret_cast<const u32x4 *>(buf + T::A_SCALE + (h * T::BM + row) * 16);
+    fr.sc[i] = *reinterpret_cast<const u32x4 *>(buf + T::A_SCALE + (h * kScaleRows + row) * 16);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       fr.c[s][i] = *reinterpret_cast<const u32x4 *>(buf + T::A_CODE + ((2 * s + h) * (T::BM + kPadRows) + row) * 16);
@@ -206,7 +210,7 @@ __device__ __forceinline__ void frag_read(Frag<WM + WN> &fr, const uint8_t *buf,
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     const int row = wn * 32 * WN + 32 * j + r;
-    fr.sc[WM + j] = *reinterpret_cast<const u32x4 *>(buf + T::W_SCALE + (h * T::BN + row) * 16);
+    fr.sc[WM + j] = *reinterpret_cast<const u32x4 *>(buf + T::W_SCALE + (h * kScaleRows + row) * 16);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       fr.c[s][WM + j] = *reinterpret_cast<const u32x4 *>(buf + T::W_CODE + ((2 * s + h) * (T::BN + kPadRows) + row) * 16);
