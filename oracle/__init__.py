@@ -35,7 +35,10 @@ Parity status per function:
   nvfp4.gemm_ref         pinned (Fraction brute force, unit-scale special case,
                          global-scale linearity, block-sum form)
   nvfp4.gelu_tanh        pinned (gelu(0)=0, gelu(y)-gelu(-y)=y, large-|y| limits)
-  nvfp4.KVCacheRef       pinned (byte closed form from the pages, append ≡ quantize)
+  nvfp4.KVCacheRef       pinned (byte closed form from the pages, append ≡ quantize,
+                         hand-worked dequant with a non-power-of-two tensor scale)
+  attention.*            pinned (closed forms, torch's scaled_dot_product_attention
+                         in float64, lossless-cache identity; see that module)
   The choices of global-scale formula, scale rounding mode, reciprocal-multiply
   order, nibble order, per-append KV scale and the binary32 error order of the
   adaptive selection are fixed by definition only
@@ -64,6 +67,7 @@ from .nvfp4 import (
     kv_bytes,
     KVCacheRef,
 )
+from .attention import attention_ref, kv_attention_ref, range_tokens
 
 __all__ = [
     "E2M1_VALUES",
@@ -84,4 +88,7 @@ __all__ = [
     "gelu_tanh",
     "kv_bytes",
     "KVCacheRef",
+    "attention_ref",
+    "kv_attention_ref",
+    "range_tokens",
 ]

@@ -319,3 +319,22 @@ class KVCacheRef:
 
     def nbytes(self) -> int:
         return kv_bytes(self.n_tokens, self.H, self.D, len(self.gscale))
+
+    def values(self, tokens) -> tuple:
+        """Exact dequantised K and V (binary64) of the given token indices:
+        [len(tokens), H, D] each, E2M1 · S · g with the g of each token's
+        append (the dequant equation without any rounding)."""
+        tokens = np.asarray(tokens, dtype=np.int64)
+        if tokens.size and (tokens.min() < 0 or tokens.max() >= self.n_tokens):
+            raise ValueError("token outside the filled cache")
+        chunk = self._chunk_of(tokens)
+        out = []
+        for which, (codes, scales) in enumerate(((self.k_codes, self.k_scales),
+                                                 (self.v_codes, self.v_scales))):
+            c = unpack_nibbles(codes[tokens])                     # [T, H, D]
+            mag = E2M1_VALUES[c & 7]
+            e = np.where((c & 8) != 0, -mag, mag)
+            s = np.repeat(e4m3_decode(scales[tokens]).astype(np.float64), BLOCK, axis=2)
+            g = np.array([self.gscale[ci][which] for ci in chunk], dtype=np.float64)
+            out.append(e * s * g[:, None, None])
+        return out[0], out[1]
