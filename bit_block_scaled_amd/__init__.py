@@ -31,7 +31,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["quantize", "quantize_into", "gemm", "linear", "linear_noalloc", "linear_q", "KVCache", "NVFP4Error", "lib",
-           "gemm_tile", "workspace", "quantize_workspace_bytes", "linear_workspace_bytes",
+           "gemm_tile", "workspace", "attention_bf16", "attention_workspace_bytes", "quantize_workspace_bytes", "linear_workspace_bytes",
            "linear_q_workspace_bytes"]
 
 
@@ -283,6 +283,28 @@ class KVCache:
         check(lib().nvfp4_kv_append_ex(C.byref(self.desc), _ptr(K), _ptr(V), T, ld, qflags, _ptr(ws),
                                        ws.numel(), _stream(self.device)))
 
+    def attention(self, Q, ranges, scale=0.0, out=None, ws=None):
+        """nvfp4_kv_attention: softmax(Q·Kᵀ·scale)·V over the cache tokens of
+        ``ranges`` (a list of disjoint (start, end) pairs), K/V dequantised in
+        the kernel.  ``Q`` is bf16 [Tq, heads, 128] or a [Tq, heads·128] row
+        view (e.g. the query slice of a fused QKV output).  Returns O bf16
+        [Tq, heads, 128] (or writes ``out``)."""
+        Tq, ldq = _rows_view(Q, self.desc.heads, "Q")
+        if out is None:
+            out = torch.empty((Tq, self.desc.heads, 128), dtype=torch.bfloat16, device=Q.device)
+        To, ldo = _rows_view(out, self.desc.heads, "out")
+        if To != Tq:
+            raise ValueError("out must have Tq rows")
+        rng = [(int(a), int(b)) for a, b in ranges]
+        Tk = sum(b - a for a, b in rng)
+        arr = (C.c_int64 * (2 * len(rng)))(*[v for ab in rng for v in ab])
+        if ws is None:
+            ws = _attention_ws(Tq, self.desc.heads, max(Tk, 1), Q.device)
+        check(lib().nvfp4_kv_attention(C.byref(self.desc), _ptr(Q), Tq, ldq, arr, len(rng), float(scale),
+                                       _ptr(out), ldo, _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(Q.device)))
+        return out
+
     def reset(self):
         """Forget every token (host counters only; enqueues nothing)."""
         check(lib().nvfp4_kv_init(C.byref(self.desc)))
@@ -298,6 +320,52 @@ class KVCache:
         check(lib().nvfp4_kv_dequant(C.byref(self.desc), t0, t1, _ptr(k_out), _ptr(v_out),
                                      _stream(self.device)))
         return k_out, v_out
+
+
+def _rows_view(t, heads, name):
+    """(rows, row stride) of a bf16 [T, heads, 128] tensor or [T, heads·128] row view."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bf16 GPU tensor")
+    if t.dim() == 3:
+        if tuple(t.shape[1:]) != (heads, 128) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [T, {heads}, 128]")
+        return t.shape[0], heads * 128
+    if t.dim() == 2 and t.shape[1] == heads * 128 and t.stride(1) == 1:
+        return t.shape[0], t.stride(0)
+    raise ValueError(f"{name} must be [T, {heads}, 128] or a [T, {heads * 128}] row view")
+
+
+def attention_workspace_bytes(Tq: int, heads: int, Tk: int) -> int:
+    n = C.c_size_t()
+    check(lib().nvfp4_kv_attention_workspace(Tq, heads, Tk, C.byref(n)))
+    return n.value
+
+
+def _attention_ws(Tq, heads, Tk, device):
+    nb = attention_workspace_bytes(Tq, heads, Tk)
+    return torch.empty((nb,), dtype=torch.uint8, device=device) if nb else None
+
+
+def attention_bf16(Q, K, V, scale=0.0, out=None, ws=None):
+    """nvfp4_attention_bf16: the same attention with bf16 K and V [Tk, heads,
+    128] (or row views): the baseline of the fused NVFP4 read."""
+    Tk, ldk = _rows_view(K, K.shape[1] if K.dim() == 3 else K.shape[1] // 128, "K")
+    heads = K.shape[1] if K.dim() == 3 else K.shape[1] // 128
+    Tv, ldv = _rows_view(V, heads, "V")
+    if Tv != Tk or ldv != ldk:
+        raise ValueError("K and V must have the same rows and row stride")
+    Tq, ldq = _rows_view(Q, heads, "Q")
+    if out is None:
+        out = torch.empty((Tq, heads, 128), dtype=torch.bfloat16, device=Q.device)
+    To, ldo = _rows_view(out, heads, "out")
+    if To != Tq:
+        raise ValueError("out must have Tq rows")
+    if ws is None:
+        ws = _attention_ws(Tq, heads, Tk, Q.device)
+    check(lib().nvfp4_attention_bf16(_ptr(Q), Tq, ldq, _ptr(K), _ptr(V), Tk, ldk, heads, float(scale),
+                                     _ptr(out), ldo, _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(Q.device)))
+    return out
 
 
 def gemm_tile(M: int, N: int, K: int) -> tuple:

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <math.h>
 #include <string.h>
 
 #include <atomic>
@@ -412,6 +413,128 @@ int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1, uint16_t *
   a.elems_per_token = c->heads * c->head_dim;
   return launched(nvfp4::launch_kv_dequant(a, static_cast<hipStream_t>(stream)),
                   static_cast<hipStream_t>(stream), "kv_dequant");
+}
+
+// ---------------------------------------------------------------------------
+// Attention over the NVFP4 cache and its bf16 twin
+
+static size_t attention_ws_bytes(int64_t Tq, int64_t heads, int64_t Tk) {
+  const int64_t ns = nvfp4::attention_splits(Tq, heads, Tk);
+  const int64_t kps = nvfp4::attention_keys_per_split(Tk, ns);
+  const int64_t nsplit = (Tk + kps - 1) / kps;
+  if (nsplit <= 1) return 0;
+  const size_t rows = size_t(nsplit) * size_t(Tq) * size_t(heads);
+  return round_up(rows * 128 * sizeof(float), 256) + round_up(rows * 2 * sizeof(float), 256);
+}
+
+static int check_attn_common(const uint16_t *Q, int64_t Tq, int64_t ldq, int64_t heads, uint16_t *O,
+                             int64_t ldo, float scale, const char *who) {
+  int s;
+  if (Tq < 1) return fail(NVFP4_EINVAL, std::string(who) + ": Tq must be >= 1");
+  if (heads < 1) return fail(NVFP4_EINVAL, std::string(who) + ": heads must be >= 1");
+  if (ldq < heads * 128 || ldq % 8 || ldo < heads * 128 || ldo % 8)
+    return fail(NVFP4_EINVAL, std::string(who) + ": ldq and ldo must be >= heads*128 and multiples of 8");
+  if (Tq > kMaxElements / ldq || Tq > kMaxElements / ldo) return fail(NVFP4_EINVAL, std::string(who) + ": Tq too large");
+  if (!(scale >= 0.0f) || scale > 3.0e38f) return fail(NVFP4_EINVAL, std::string(who) + ": scale must be finite and >= 0");
+  if ((s = check_ptr(Q, "Q"))) return s;
+  if ((s = check_ptr(O, "O"))) return s;
+  return NVFP4_OK;
+}
+
+static int run_attention(nvfp4::AttnArgs &a, bool bf16, float scale, void *ws, size_t ws_bytes,
+                         void *stream, const char *who) {
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf(128.0f);
+  a.qk_scale = sc * 1.4426950408889634f;
+  const int64_t ns = nvfp4::attention_splits(a.Tq, a.heads, a.Tk);
+  a.keys_per_split = nvfp4::attention_keys_per_split(a.Tk, ns);
+  a.nsplit = (int)((a.Tk + a.keys_per_split - 1) / a.keys_per_split);
+  const size_t need = attention_ws_bytes(a.Tq, a.heads, a.Tk);
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (a.nsplit > 1) {
+    if (ws == nullptr || ws_bytes < need) return fail(NVFP4_EWORKSPACE, std::string(who) + ": workspace too small");
+    int s;
+    if ((s = check_ptr(ws, "ws"))) return s;
+    const size_t rows = size_t(a.nsplit) * size_t(a.Tq) * size_t(a.heads);
+    a.part_o = static_cast<float *>(ws);
+    a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round_up(rows * 128 * sizeof(float), 256));
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(nvfp4::launch_attention(a, bf16, st), st, who);
+}
+
+int nvfp4_kv_attention_workspace(int64_t Tq, int64_t heads, int64_t Tk, size_t *bytes) {
+  if (bytes == nullptr) return fail(NVFP4_EINVAL, "bytes is NULL");
+  if (Tq < 1 || heads < 1 || Tk < 1) return fail(NVFP4_EINVAL, "kv_attention_workspace: Tq, heads and Tk must be >= 1");
+  if (Tq > kMaxElements / (heads * 128)) return fail(NVFP4_EINVAL, "kv_attention_workspace: Tq too large");
+  *bytes = attention_ws_bytes(Tq, heads, Tk);
+  return NVFP4_OK;
+}
+
+int nvfp4_kv_attention(const nvfp4_kv_cache *c, const uint16_t *Q, int64_t Tq, int64_t ldq,
+                       const int64_t *ranges, int n_ranges, float scale, uint16_t *O, int64_t ldo,
+                       void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_cache(c, "kv_attention"))) return s;
+  if (c->head_dim != 128) return fail(NVFP4_EINVAL, "kv_attention: head_dim must be 128");
+  if ((s = check_attn_common(Q, Tq, ldq, c->heads, O, ldo, scale, "kv_attention"))) return s;
+  if (ranges == nullptr || n_ranges < 1 || n_ranges > NVFP4_ATTN_MAX_RANGES)
+    return fail(NVFP4_EINVAL, "kv_attention: between 1 and NVFP4_ATTN_MAX_RANGES token ranges are required");
+  nvfp4::AttnArgs a{};
+  int64_t Tk = 0;
+  for (int i = 0; i < n_ranges; ++i) {
+    const int64_t lo = ranges[2 * i], hi = ranges[2 * i + 1];
+    if (lo < 0 || hi <= lo || hi > c->n_tokens)
+      return fail(NVFP4_EINVAL, "kv_attention: each range must be a non-empty [start, end) inside the filled cache");
+    for (int j = 0; j < i; ++j)
+      if (lo < ranges[2 * j + 1] && ranges[2 * j] < hi) return fail(NVFP4_EINVAL, "kv_attention: ranges overlap");
+    a.range_lo[i] = lo;
+    a.range_len[i] = hi - lo;
+    Tk += hi - lo;
+  }
+  a.n_ranges = n_ranges;
+  a.Tk = Tk;
+  a.q = Q;
+  a.ldq = ldq;
+  a.o = O;
+  a.ldo = ldo;
+  a.Tq = Tq;
+  a.heads = c->heads;
+  a.kc = c->k_codes;
+  a.ks = c->k_scales;
+  a.vc = c->v_codes;
+  a.vs = c->v_scales;
+  a.gscale = c->gscale;
+  a.chunk_start = c->chunk_start;
+  a.n_chunks = c->n_chunks;
+  return run_attention(a, false, scale, ws, ws_bytes, stream, "kv_attention");
+}
+
+int nvfp4_attention_bf16(const uint16_t *Q, int64_t Tq, int64_t ldq, const uint16_t *K, const uint16_t *V,
+                         int64_t Tk, int64_t ldkv, int64_t heads, float scale, uint16_t *O, int64_t ldo,
+                         void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_attn_common(Q, Tq, ldq, heads, O, ldo, scale, "attention_bf16"))) return s;
+  if (Tk < 1) return fail(NVFP4_EINVAL, "attention_bf16: Tk must be >= 1");
+  if (ldkv < heads * 128 || ldkv % 8) return fail(NVFP4_EINVAL, "attention_bf16: ldkv must be >= heads*128 and a multiple of 8");
+  if (Tk > kMaxElements / ldkv) return fail(NVFP4_EINVAL, "attention_bf16: Tk too large");
+  if ((s = check_ptr(K, "K"))) return s;
+  if ((s = check_ptr(V, "V"))) return s;
+  nvfp4::AttnArgs a{};
+  a.range_lo[0] = 0;
+  a.range_len[0] = Tk;
+  a.n_ranges = 1;
+  a.Tk = Tk;
+  a.q = Q;
+  a.ldq = ldq;
+  a.o = O;
+  a.ldo = ldo;
+  a.Tq = Tq;
+  a.heads = heads;
+  a.kb = K;
+  a.vb = V;
+  a.ldkv = ldkv;
+  return run_attention(a, true, scale, ws, ws_bytes, stream, "attention_bf16");
 }
 
 uint64_t nvfp4_testing_set_quantize_wait(uint64_t ticks) { return nvfp4::set_resident_wait_ticks(ticks); }

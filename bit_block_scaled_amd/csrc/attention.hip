@@ -1,0 +1,467 @@
+// Attention over the NVFP4 KV cache, fused with its dequantisation (gfx950),
+// and a bf16-K/V twin of the same kernel as the baseline.
+//
+// Method: "LongLive-2.0：用 NVFP4 并行底座做长视频生成", 二、方法 / 推理底座 (the KV
+// cache is stored in NVFP4 and read back through a dequant kernel inside
+// inference, overhead within 2 %) and 二、方法 / 多镜头注意力锚点 (a chunk attends
+// to the global-sink frames, the shot-sink frames and a recent window:
+// disjoint token ranges of the cache).  O = softmax(Q·Kᵀ·scale)·V per head.
+//
+// Work split: a workgroup owns 128 queries (4 waves x 32) of one head and one
+// split of the keys; it walks its keys in tiles of 64.  Each tile is decoded
+// once by the whole workgroup into LDS:
+//   K as fp16 [key][d] (E2M1 · E4M3 is exact in fp16: the GEMM's convert-and-
+//     scale decode), rows padded to 272 B so the fragment reads of 8 lanes
+//     hit distinct banks;
+//   V transposed, bf16 [d][key] (E2M1 · E4M3 exact in bf16 as well), rows
+//     padded to 136 B;
+//   the per-key factors g_K · scale · log2(e) and g_V of each key's append.
+// Scores are computed transposed, Sᵀ = K·Qᵀ (v_mfma_f32_32x32x16_f16, Q
+// converted from bf16 to fp16 once), so a lane holds 32 of one query's 64
+// scores and the other 32 sit in the lane 32 apart: the row maximum is an
+// in-lane reduction plus one exchange.  Online softmax in base 2 (exp2), P
+// times g_V rounded to bf16 (bf16 keeps the exponent range of small
+// probabilities), then Oᵀ += Vᵀ·Pᵀ (v_mfma_f32_32x32x16_bf16): the
+// accumulator registers of Sᵀ are already laid out as the B operand of that
+// product for the key order k = 16s + 8(i/4) + 4h + i%4, which the Vᵀ
+// fragment reads follow.  The tile after the current one is fetched from
+// global memory into registers while the current one is computed.
+// With more than one split, each split writes its unnormalised O with its
+// running maximum and sum, and k_attn_combine merges them.
+//
+// The twin (BF16) copies bf16 K and V into the same LDS layout (K kept as
+// bf16, Sᵀ on the bf16 MFMA); everything else is the same code.
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+
+constexpr int kAD = 128;                  // head_dim
+constexpr int kAQ = 128;                  // queries per workgroup
+constexpr int kAK = 64;                   // keys per tile
+constexpr int kAThreads = 256;
+constexpr int kKRow = kAD * 2 + 16;       // LDS bytes per K row (272)
+constexpr int kVRow = kAK * 2 + 8;        // LDS bytes per Vᵀ row (136)
+constexpr int kAttnLdsStarts = 2048;      // chunk starts kept in LDS (as int32)
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+struct AttnLds {
+  uint8_t k[kAK * kKRow];
+  uint8_t v[kAD * kVRow];
+  float gk[kAK], gv[kAK];
+  int32_t starts[kAttnLdsStarts];
+};
+
+// Token of virtual key j (the concatenated ranges), or -1 past the keys.
+__device__ __forceinline__ int64_t key_token(const AttnArgs &a, int64_t j) {
+  int64_t tok = -1;
+#pragma unroll
+  for (int r = 0; r < kAttnMaxRanges; ++r) {
+    if (r < a.n_ranges && tok < 0) {
+      if (j < a.range_len[r]) tok = a.range_lo[r] + j;
+      j -= a.range_len[r];
+    }
+  }
+  return tok;
+}
+
+// Append (chunk) index of token `tok`: starts[c] <= tok < starts[c + 1].
+template <typename P>
+__device__ __forceinline__ int64_t attn_chunk_of(P starts, int64_t n_chunks, int64_t tok) {
+  int64_t lo = 0, hi = n_chunks - 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if ((int64_t)starts[mid] <= tok) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One tile's global data in flight, per thread.
+//   K part: key kk = t % 64, quarter c = t / 64 (elements 32c .. 32c+31);
+//   V part: key pair kp = t % 32 (keys 2kp, 2kp+1), d-block db = t / 32
+//   (elements 16db .. 16db+15); meta: threads t < 64, the token of key t.
+template <bool BF16>
+struct TileIn;
+template <>
+struct TileIn<false> {
+  u32x4 kcode;
+  uint32_t kscale;          // two scale bytes
+  u32x2 vcode[2];
+  uint32_t vscale[2];
+  int64_t tok;
+};
+template <>
+struct TileIn<true> {
+  u32x4 kraw[4];            // 32 bf16
+  u32x4 vraw[2][2];         // 16 bf16 per key
+  int64_t tok;
+};
+
+template <bool BF16>
+__device__ __forceinline__ void tile_fetch(TileIn<BF16> &f, const AttnArgs &a, int h, int64_t j0,
+                                           int64_t j1) {
+  const int t = threadIdx.x;
+  const int kk = t & 63, c = t >> 6, kp = t & 31, db = t >> 5;
+  const int64_t HD = a.heads * kAD;
+  {
+    const int64_t j = j0 + kk;
+    const int64_t tok = j < j1 ? key_token(a, j) : -1;
+    if constexpr (!BF16) {
+      f.kcode = u32x4{0u, 0u, 0u, 0u};
+      f.kscale = 0u;
+      if (tok >= 0) {
+        const int64_t e = tok * HD + (int64_t)h * kAD;             // element index of the row
+        f.kcode = *reinterpret_cast<const u32x4 *>(a.kc + e / 2 + 16 * c);
+        f.kscale = *reinterpret_cast<const uint16_t *>(a.ks + e / 16 + 2 * c);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.kraw[i] = u32x4{0u, 0u, 0u, 0u};
+      if (tok >= 0) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.kb + tok * a.ldkv + (int64_t)h * kAD + 32 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.kraw[i] = p[i];
+      }
+    }
+    f.tok = tok;
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t j = j0 + 2 * kp + q;
+    const int64_t tok = j < j1 ? key_token(a, j) : -1;
+    if constexpr (!BF16) {
+      f.vcode[q] = u32x2{0u, 0u};
+      f.vscale[q] = 0u;
+      if (tok >= 0) {
+        const int64_t e = tok * HD + (int64_t)h * kAD;
+        f.vcode[q] = *reinterpret_cast<const u32x2 *>(a.vc + e / 2 + 8 * db);
+        f.vscale[q] = a.vs[e / 16 + db];
+      }
+    } else {
+      f.vraw[q][0] = f.vraw[q][1] = u32x4{0u, 0u, 0u, 0u};
+      if (tok >= 0) {
+        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.vb + tok * a.ldkv + (int64_t)h * kAD + 16 * db);
+        f.vraw[q][0] = p[0];
+        f.vraw[q][1] = p[1];
+      }
+    }
+  }
+}
+
+// fp16 E2M1 · S of 8 codes: E2M1 · 2^8 by the converter, times S · 2^-8 (the
+// fp16 pattern of S·2^-8 is the E4M3 byte shifted left by 7).
+__device__ __forceinline__ f16x8 attn_decode8_f16(uint32_t w, uint32_t sbyte) {
+  const f16x2 s = __builtin_bit_cast(f16x2, (sbyte & 0xFFu) * 0x00800080u);
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s;
+  const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// E2M1 · S of 8 codes in binary32 (exact).
+__device__ __forceinline__ void attn_decode8_f32(uint32_t w, float s, float (&o)[8]) {
+  const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  o[0] = e0.x * s; o[1] = e0.y * s; o[2] = e1.x * s; o[3] = e1.y * s;
+  o[4] = e2.x * s; o[5] = e2.y * s; o[6] = e3.x * s; o[7] = e3.y * s;
+}
+
+// Writes one fetched tile into LDS (K rows, Vᵀ rows, per-key factors).
+template <bool BF16>
+__device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnLds &L, const AttnArgs &a,
+                                           bool starts_in_lds) {
+  const int t = threadIdx.x;
+  const int kk = t & 63, c = t >> 6, kp = t & 31, db = t >> 5;
+  uint8_t *krow = L.k + kk * kKRow + 64 * c;
+  if constexpr (!BF16) {
+    const uint32_t s0 = f.kscale & 0xFFu, s1 = (f.kscale >> 8) & 0xFFu;
+    *reinterpret_cast<f16x8 *>(krow + 0) = attn_decode8_f16(f.kcode.x, s0);
+    *reinterpret_cast<f16x8 *>(krow + 16) = attn_decode8_f16(f.kcode.y, s0);
+    *reinterpret_cast<f16x8 *>(krow + 32) = attn_decode8_f16(f.kcode.z, s1);
+    *reinterpret_cast<f16x8 *>(krow + 48) = attn_decode8_f16(f.kcode.w, s1);
+    float v0[16], v1[16];
+    {
+      const float sa = e4m3_decode(f.vscale[0]), sb = e4m3_decode(f.vscale[1]);
+      float tmp[8];
+      attn_decode8_f32(f.vcode[0].x, sa, tmp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v0[i] = tmp[i];
+      attn_decode8_f32(f.vcode[0].y, sa, tmp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v0[8 + i] = tmp[i];
+      attn_decode8_f32(f.vcode[1].x, sb, tmp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v1[i] = tmp[i];
+      attn_decode8_f32(f.vcode[1].y, sb, tmp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v1[8 + i] = tmp[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      *reinterpret_cast<uint32_t *>(L.v + (16 * db + i) * kVRow + 4 * kp) = pack_bf16x2(v0[i], v1[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(krow + 16 * i) = f.kraw[i];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t w0 = f.vraw[0][i >> 3][(i >> 1) & 3], w1 = f.vraw[1][i >> 3][(i >> 1) & 3];
+      // (key 2kp, d) in the low half, (key 2kp+1, d) in the high half
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+      *reinterpret_cast<uint32_t *>(L.v + (16 * db + i) * kVRow + 4 * kp) =
+          __builtin_amdgcn_perm(w1, w0, sel);
+    }
+  }
+  if (t < kAK) {
+    float gk = 0.0f, gv = 0.0f;
+    if (f.tok >= 0) {
+      if constexpr (!BF16) {
+        const int64_t ci = starts_in_lds ? attn_chunk_of(L.starts, a.n_chunks, f.tok)
+                                         : attn_chunk_of(a.chunk_start, a.n_chunks, f.tok);
+        gk = a.gscale[2 * ci] * a.qk_scale;
+        gv = a.gscale[2 * ci + 1];
+      } else {
+        gk = a.qk_scale;
+        gv = 1.0f;
+      }
+    }
+    L.gk[t] = gk;
+    L.gv[t] = gv;
+  }
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t attn_smem[];
+  AttnLds &L = *reinterpret_cast<AttnLds *>(attn_smem);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 31, hh = lane >> 5;
+  const int h = blockIdx.y, split = blockIdx.z;
+  const int64_t q = (int64_t)blockIdx.x * kAQ + 32 * w + r;       // this lane's query
+  const int64_t qc = q < a.Tq ? q : a.Tq - 1;
+  const int64_t j0 = (int64_t)split * a.keys_per_split;
+  const int64_t j1 = (j0 + a.keys_per_split < a.Tk) ? j0 + a.keys_per_split : a.Tk;
+
+  bool starts_in_lds = false;
+  if constexpr (!BF16) {
+    starts_in_lds = a.n_chunks < kAttnLdsStarts;
+    if (starts_in_lds)
+      for (int64_t i = threadIdx.x; i <= a.n_chunks; i += kAThreads) L.starts[i] = (int32_t)a.chunk_start[i];
+  }
+
+  // query fragments: lane (r, hh) holds d = 16·step + 8·hh .. +7 of query q
+  typedef typename std::conditional<BF16, bf16x8, f16x8>::type QFrag;
+  QFrag qf[8];
+  {
+    const u32x4 *qp = reinterpret_cast<const u32x4 *>(a.q + qc * a.ldq + (int64_t)h * kAD + 8 * hh);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 raw = qp[2 * s];
+      if constexpr (BF16) {
+        qf[s] = __builtin_bit_cast(bf16x8, raw);
+      } else {
+        f16x8 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wv = raw[e];
+          x[2 * e] = (_Float16)bf16_bits_to_f32(wv & 0xFFFFu);
+          x[2 * e + 1] = (_Float16)bf16_bits_to_f32(wv >> 16);
+        }
+        qf[s] = x;
+      }
+    }
+  }
+
+  float m = -__builtin_huge_valf(), l = 0.0f;
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[i][v] = 0.0f;
+
+  TileIn<BF16> fin;
+  tile_fetch<BF16>(fin, a, h, j0, j1);
+  if constexpr (!BF16) {
+    if (starts_in_lds) __syncthreads();
+  }
+  for (int64_t jt = j0; jt < j1; jt += kAK) {
+    tile_store<BF16>(fin, L, a, starts_in_lds);
+    __syncthreads();
+    const int kvalid = (j1 - jt) < kAK ? (int)(j1 - jt) : kAK;
+    if (jt + kAK < j1) tile_fetch<BF16>(fin, a, h, jt + kAK, j1);
+
+    // Sᵀ = K·Qᵀ: lane (query r, hh) gets keys 32kb + 8(v/4) + 4hh + v%4
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const uint8_t *kr = L.k + (32 * kb + r) * kKRow + 16 * hh;
+      f32x16 acc = {};
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const u32x4 raw = *reinterpret_cast<const u32x4 *>(kr + 32 * st);
+        if constexpr (BF16)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), qf[st], acc, 0, 0, 0);
+        else
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, raw), qf[st], acc, 0, 0, 0);
+      }
+      s[kb] = acc;
+    }
+    // scale by each key's g_K · scale · log2(e); mask keys past the split
+    float mt = -__builtin_huge_valf();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int key0 = 32 * kb + 8 * g4 + 4 * hh;
+        const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&L.gk[key0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float tv = s[kb][4 * g4 + e] * gk4[e];
+          if (kvalid < kAK && key0 + e >= kvalid) tv = -__builtin_huge_valf();
+          s[kb][4 * g4 + e] = tv;
+          mt = mt > tv ? mt : tv;
+        }
+      }
+    {
+      const float other = __shfl_xor(mt, 32, 64);
+      mt = mt > other ? mt : other;
+    }
+    const float m_new = m > mt ? m : mt;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][v] - m_new);
+        s[kb][v] = p;
+        psum += p;
+      }
+    l = l * alpha + psum;
+    m = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+    }
+    // Pᵀ fragments (times each key's g_V, rounded to bf16): slice sl holds
+    // keys 16sl + 8(i/4) + 4hh + i%4 for i = 0..7, registers 8(sl%2) + i of s[sl/2]
+    bf16x8 pf[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int kb = sl >> 1, v0 = 8 * (sl & 1);
+      const f32x4 ga = *reinterpret_cast<const f32x4 *>(&L.gv[32 * kb + 8 * (v0 / 4) + 4 * hh]);
+      const f32x4 gb = *reinterpret_cast<const f32x4 *>(&L.gv[32 * kb + 8 * (v0 / 4 + 1) + 4 * hh]);
+      u32x4 pk;
+      pk.x = pack_bf16x2(s[kb][v0 + 0] * ga[0], s[kb][v0 + 1] * ga[1]);
+      pk.y = pack_bf16x2(s[kb][v0 + 2] * ga[2], s[kb][v0 + 3] * ga[3]);
+      pk.z = pack_bf16x2(s[kb][v0 + 4] * gb[0], s[kb][v0 + 5] * gb[1]);
+      pk.w = pack_bf16x2(s[kb][v0 + 6] * gb[2], s[kb][v0 + 7] * gb[3]);
+      pf[sl] = __builtin_bit_cast(bf16x8, pk);
+    }
+    // Oᵀ += Vᵀ·Pᵀ: lane (d = 32db + r, hh) reads keys 16sl + 4hh .. +3 and 16sl + 8 + 4hh .. +3
+#pragma unroll
+    for (int dbk = 0; dbk < 4; ++dbk) {
+      const uint8_t *vr = L.v + (32 * dbk + r) * kVRow + 8 * hh;
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 32 * sl);
+        const u32x2 hi = *reinterpret_cast<const u32x2 *>(vr + 32 * sl + 16);
+        const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
+        o[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[sl], o[dbk], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // both half-waves hold the same query; their sums cover disjoint keys
+  const float lt = l + __shfl_xor(l, 32, 64);
+  if (q >= a.Tq) return;
+  if (a.part_o == nullptr) {
+    const float inv = 1.0f / lt;
+    uint16_t *orow = a.o + q * a.ldo + (int64_t)h * kAD;
+#pragma unroll
+    for (int dbk = 0; dbk < 4; ++dbk)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * dbk + 8 * g4 + 4 * hh;
+        const u32x2 pk = {pack_bf16x2(o[dbk][4 * g4] * inv, o[dbk][4 * g4 + 1] * inv),
+                          pack_bf16x2(o[dbk][4 * g4 + 2] * inv, o[dbk][4 * g4 + 3] * inv)};
+        *reinterpret_cast<u32x2 *>(orow + d) = pk;
+      }
+  } else {
+    const int64_t row = ((int64_t)split * a.Tq + q) * a.heads + h;
+    float *po = a.part_o + row * kAD;
+#pragma unroll
+    for (int dbk = 0; dbk < 4; ++dbk)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * dbk + 8 * g4 + 4 * hh;
+        *reinterpret_cast<f32x4 *>(po + d) =
+            f32x4{o[dbk][4 * g4], o[dbk][4 * g4 + 1], o[dbk][4 * g4 + 2], o[dbk][4 * g4 + 3]};
+      }
+    if (hh == 0) *reinterpret_cast<f32x2 *>(a.part_ml + 2 * row) = f32x2{m, lt};
+  }
+}
+
+// Merges the splits of one (query, head) row per 128 threads (one per d):
+// O = Σ_s O_s · 2^(m_s − M) / Σ_s l_s · 2^(m_s − M), M = max_s m_s.
+__global__ void __launch_bounds__(kAThreads) k_attn_combine(AttnArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);       // q·heads + h
+  const int d = threadIdx.x & 127;
+  if (row >= a.Tq * a.heads) return;
+  const int64_t rows = a.Tq * a.heads;
+  float M = -__builtin_huge_valf();
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ms = a.part_ml[2 * (s * rows + row)];
+    M = M > ms ? M : ms;
+  }
+  float num = 0.0f, den = 0.0f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float ms = a.part_ml[2 * (s * rows + row)], ls = a.part_ml[2 * (s * rows + row) + 1];
+    const float wgt = __builtin_amdgcn_exp2f(ms - M);
+    num += a.part_o[(s * rows + row) * kAD + d] * wgt;
+    den += ls * wgt;
+  }
+  const int64_t qi = row / a.heads, h = row - qi * a.heads;
+  const float val = num / den;
+  a.o[qi * a.ldo + h * kAD + d] = (uint16_t)(pack_bf16x2(val, 0.0f) & 0xFFFFu);
+}
+
+int64_t attention_splits(int64_t Tq, int64_t heads, int64_t Tk) {
+  const int64_t tiles = ((Tq + kAQ - 1) / kAQ) * heads;
+  int64_t want = (512 + tiles - 1) / tiles;                   // at least ~512 workgroups
+  int64_t most = Tk / (8 * kAK);                              // at least 8 key tiles per split
+  if (most > 32) most = 32;
+  if (want > most) want = most;
+  return want < 1 ? 1 : want;
+}
+
+int64_t attention_keys_per_split(int64_t Tk, int64_t nsplit) {
+  const int64_t per = (Tk + nsplit - 1) / nsplit;
+  return (per + kAK - 1) / kAK * kAK;
+}
+
+hipError_t launch_attention(const AttnArgs &a, bool bf16, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.Tq + kAQ - 1) / kAQ), (unsigned)a.heads, (unsigned)a.nsplit);
+  const size_t lds = sizeof(AttnLds);
+  if (bf16)
+    hipLaunchKernelGGL(k_attention<true>, grid, dim3(kAThreads), lds, stream, a);
+  else
+    hipLaunchKernelGGL(k_attention<false>, grid, dim3(kAThreads), lds, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.part_o == nullptr) return e;
+  const int64_t rows = a.Tq * a.heads;
+  hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)((rows + 1) / 2)), dim3(kAThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -103,4 +103,35 @@ struct KvDequantArgs {
 
 hipError_t launch_kv_dequant(const KvDequantArgs &a, hipStream_t stream);
 
+// Attention of bf16 queries over keys/values from the NVFP4 cache (or, for the
+// bf16 twin, from bf16 K/V tensors).  head_dim is 128.  Keys are the tokens of
+// up to kAttnMaxRanges disjoint ranges, concatenated ("virtual keys"
+// 0 .. Tk-1); the workgroups split them into nsplit parts of keys_per_split
+// keys (a multiple of 64); with nsplit > 1, part_o [nsplit][Tq][heads][128]
+// and part_ml [nsplit][Tq][heads][2] hold the partial results.
+constexpr int kAttnMaxRanges = 4;
+struct AttnArgs {
+  const uint16_t *q;            // bf16, query t head h at q + t·ldq + 128·h
+  int64_t ldq;
+  uint16_t *o;                  // bf16 output, same layout with ldo
+  int64_t ldo;
+  int64_t Tq, heads;
+  const uint8_t *kc, *ks, *vc, *vs;     // NVFP4 cache codes / scales
+  const float *gscale;
+  const int64_t *chunk_start;
+  int64_t n_chunks;
+  const uint16_t *kb, *vb;              // bf16 twin: token t head h at kb + t·ldkv + 128·h
+  int64_t ldkv;
+  int64_t range_lo[kAttnMaxRanges], range_len[kAttnMaxRanges];
+  int n_ranges;
+  int64_t Tk;
+  float qk_scale;               // scale · log2(e)
+  int nsplit;
+  int64_t keys_per_split;
+  float *part_o, *part_ml;
+};
+int64_t attention_splits(int64_t Tq, int64_t heads, int64_t Tk);
+int64_t attention_keys_per_split(int64_t Tk, int64_t nsplit);
+hipError_t launch_attention(const AttnArgs &a, bool bf16, hipStream_t stream);
+
 }  // namespace nvfp4

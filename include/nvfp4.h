@@ -289,6 +289,49 @@ int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, 
 int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1,
                      uint16_t *K_out, uint16_t *V_out, void *stream);
 
+/*
+ * Attention of a chunk of queries over the NVFP4 KV cache, with the cache's
+ * dequantisation fused into the kernel.  Source: 二、方法 / 推理底座 (the KV
+ * cache is kept in NVFP4 and dequantised by a hand-written kernel inside
+ * inference) and 二、方法 / 多镜头注意力锚点 (the KV set of a chunk is the
+ * global-sink frames, the shot-sink frames and a window of recent frames,
+ * without duplicates).  For each head h and query i:
+ *   O[i, h] = softmax_j( Q[i, h] · K[j, h] · scale ) · V[j, h]
+ * over the tokens j of `ranges`, with K and V the exact dequantised values
+ * E2M1 · E4M3 · g of each token's append.
+ *   c        cache with head_dim 128 (others: NVFP4_EINVAL)
+ *   Q        bf16: query i, head h at Q + i·ldq + 128·h (ldq >= heads·128,
+ *            ldq % 8 == 0; Q may be the query slice of a fused QKV output)
+ *   ranges   host array of n_ranges (1..NVFP4_ATTN_MAX_RANGES) pairs
+ *            [start, end) of disjoint, non-empty token ranges inside the
+ *            filled cache; their tokens form the keys, in order
+ *   scale    softmax scale; 0 means 1/sqrt(128)
+ *   O        out, bf16, same layout as Q with ldo
+ *   ws       scratch of nvfp4_kv_attention_workspace(Tq, heads, Tk) bytes
+ *            (Tk = total tokens of the ranges; may be 0 bytes, then ws may be
+ *            NULL); it needs no initialisation
+ * Arithmetic: Q converted to fp16 (exact for |q| in [2^-14, 65504] or 0),
+ * K·Q products exact and summed in fp32, times g_K·scale, base-2 online
+ * softmax in fp32, P·g_V rounded to bf16, products with V (exact) summed in
+ * fp32, one bf16 rounding of the output.  Requires |q| < 65504.
+ */
+#define NVFP4_ATTN_MAX_RANGES 4
+int nvfp4_kv_attention_workspace(int64_t Tq, int64_t heads, int64_t Tk, size_t *bytes);
+int nvfp4_kv_attention(const nvfp4_kv_cache *c, const uint16_t *Q, int64_t Tq, int64_t ldq,
+                       const int64_t *ranges, int n_ranges, float scale,
+                       uint16_t *O, int64_t ldo, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The same attention with bf16 K and V tensors instead of the NVFP4 cache
+ * (token j, head h at K + j·ldkv + 128·h): the baseline against which the
+ * fused dequantisation's cost is measured.  Q·K and P·V on the bf16 matrix
+ * cores (P rounded to bf16), otherwise as nvfp4_kv_attention; the workspace
+ * size is nvfp4_kv_attention_workspace(Tq, heads, Tk).
+ */
+int nvfp4_attention_bf16(const uint16_t *Q, int64_t Tq, int64_t ldq, const uint16_t *K,
+                         const uint16_t *V, int64_t Tk, int64_t ldkv, int64_t heads, float scale,
+                         uint16_t *O, int64_t ldo, void *ws, size_t ws_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *nvfp4_strerror(int status);
 
