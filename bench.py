@@ -21,8 +21,10 @@ event after every kernel (the library's launch-event testing hook), which
 gives the per-kernel breakdown and the dominant kernel's roofline (the up
 GEMM).  Further entries in `kernels` time the other configurations' kernels
 (QKV and long-context GEMMs and quantisers, the 65536-token KV append
-sequence and its read-back, a 1 GiB device copy) with p10/p50/p90 over
-repetitions; the HBM-bound ones after a 1 GiB cache flush ("cold").
+sequence and its read-back, attention of an 880-token query chunk over that
+cache read in NVFP4 against the same kernel on bf16 K/V, a 1 GiB device
+copy) with p10/p50/p90 over repetitions; the HBM-bound ones after a 1 GiB
+cache flush ("cold").
 `cpu_baseline` is the CPU oracle on a bounded sample of the FFN step.
 
 Other modes: --copy-only (1 GiB copy, for rocprofv3 counter calibration),
@@ -480,7 +482,45 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
     t = time_us(torch, lambda: cache.dequant(0, T, ko, vo), 100, 5, flush)
     kernels["kv65536_dequant_cold"] = {"tokens": T, "us": pct(t),
                                        "roofline": roof_hbm(2 * T * 3072 * Q_BYTES_PER_ELEM, float(np.median(t)))}
-    del kd, vd, cache, ko, vo
+    # attention of one 880-token query chunk over the cache (24 heads of 128):
+    # the NVFP4 cache read inside the kernel, against the bf16 twin on the
+    # cache's bf16 read-back, and against the read-back followed by the twin
+    log("extras: attention over the NVFP4 cache vs bf16 K/V")
+    del kd, vd
+    torch.cuda.empty_cache()
+    cache.dequant(0, T, ko, vo)
+    rng = np.random.default_rng(5)
+    qa = up(workloads.to_bf16_bits(rng.standard_normal((880, 24, 128)).astype(np.float32)))
+    oa = torch.empty_like(qa)
+    for name, ranges in (("full", [(0, T)]), ("sink_window", [(0, 880), (T - 8800, T)])):
+        Tk = sum(b - a for a, b in ranges)
+        ws_a = nv._attention_ws(880, 24, Tk, dev)
+        flops_a = 4.0 * 880 * Tk * 24 * 128
+        tn = time_us(torch, lambda: cache.attention(qa, ranges, out=oa, ws=ws_a), 10, 3)
+        if name == "full":
+            kb, vb = ko, vo
+        else:
+            kb = torch.cat([ko[a:b] for a, b in ranges]).contiguous()
+            vb = torch.cat([vo[a:b] for a, b in ranges]).contiguous()
+        tb = time_us(torch, lambda: nv.attention_bf16(qa, kb, vb, out=oa, ws=ws_a), 10, 3)
+
+        offs = np.r_[0, np.cumsum([b - a for a, b in ranges])]
+
+        def unfused():                   # read the key ranges back to bf16, then the twin
+            for i, (a, b) in enumerate(ranges):
+                cache.dequant(a, b, kb[offs[i]:offs[i + 1]], vb[offs[i]:offs[i + 1]])
+            nv.attention_bf16(qa, kb, vb, out=oa, ws=ws_a)
+        tu = time_us(torch, unfused, 10, 3)
+        pn, pb, pu = float(np.median(tn)), float(np.median(tb)), float(np.median(tu))
+        kernels[f"attention_{name}_nvfp4"] = {"queries": 880, "keys": Tk, "heads": 24, "us": pct(tn),
+                                             "roofline": roof_gemm(flops_a, pn)}
+        kernels[f"attention_{name}_bf16_twin"] = {"queries": 880, "keys": Tk, "heads": 24, "us": pct(tb),
+                                                 "roofline": roof_gemm(flops_a, pb)}
+        kernels[f"attention_{name}_dequant_then_bf16"] = {"us": pct(tu)}
+        kernels[f"attention_{name}_nvfp4_vs_bf16"] = {"time_ratio": round(pn / pb, 4),
+                                                       "dequant_then_bf16_ratio": round(pu / pb, 4)}
+        del ws_a
+    del cache, ko, vo, qa, oa
     torch.cuda.empty_cache()
     return round(float(copy_gbs), 1)
 

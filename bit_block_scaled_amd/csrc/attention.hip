@@ -25,7 +25,8 @@
 // accumulator registers of Sᵀ are already laid out as the B operand of that
 // product for the key order k = 16s + 8(i/4) + 4h + i%4, which the Vᵀ
 // fragment reads follow.  The tile after the current one is fetched from
-// global memory into registers while the current one is computed.
+// global memory into registers while the current one is computed; the
+// decoded tiles alternate between two LDS buffers, one barrier per tile.
 // With more than one split, each split writes its unnormalised O with its
 // running maximum and sum, and k_attn_combine merges them.
 //
@@ -48,11 +49,25 @@ constexpr int kAttnLdsStarts = 2048;      // chunk starts kept in LDS (as int32)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
-struct AttnLds {
+// One decoded key tile.  The workgroup keeps two: it decodes tile i+1 into
+// one while its waves read tile i from the other, so one barrier per tile
+// orders both.
+struct AttnTile {
   uint8_t k[kAK * kKRow];
   uint8_t v[kAD * kVRow];
   float gk[kAK], gv[kAK];
+};
+struct AttnLds {
+  AttnTile buf[2];
   int32_t starts[kAttnLdsStarts];
+};
+
+// The append that the previous key of this thread's slot belonged to, with
+// its factors: consecutive tiles move each slot's token forward by 64, so the
+// append only has to be searched again when a token leaves [lo, hi).
+struct ChunkCache {
+  int64_t lo = 0, hi = 0;
+  float gk = 0.0f, gv = 0.0f;
 };
 
 // Token of virtual key j (the concatenated ranges), or -1 past the keys.
@@ -176,8 +191,8 @@ __device__ __forceinline__ void attn_decode8_f32(uint32_t w, float s, float (&o)
 
 // Writes one fetched tile into LDS (K rows, Vᵀ rows, per-key factors).
 template <bool BF16>
-__device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnLds &L, const AttnArgs &a,
-                                           bool starts_in_lds) {
+__device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, const int32_t *lds_starts,
+                                           ChunkCache &cc, const AttnArgs &a) {
   const int t = threadIdx.x;
   const int kk = t & 63, c = t >> 6, kp = t & 31, db = t >> 5;
   uint8_t *krow = L.k + kk * kKRow + 64 * c;
@@ -223,10 +238,16 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnLds &L, co
     float gk = 0.0f, gv = 0.0f;
     if (f.tok >= 0) {
       if constexpr (!BF16) {
-        const int64_t ci = starts_in_lds ? attn_chunk_of(L.starts, a.n_chunks, f.tok)
-                                         : attn_chunk_of(a.chunk_start, a.n_chunks, f.tok);
-        gk = a.gscale[2 * ci] * a.qk_scale;
-        gv = a.gscale[2 * ci + 1];
+        if (f.tok < cc.lo || f.tok >= cc.hi) {
+          const int64_t ci = lds_starts != nullptr ? attn_chunk_of(lds_starts, a.n_chunks, f.tok)
+                                                   : attn_chunk_of(a.chunk_start, a.n_chunks, f.tok);
+          cc.lo = lds_starts != nullptr ? (int64_t)lds_starts[ci] : a.chunk_start[ci];
+          cc.hi = lds_starts != nullptr ? (int64_t)lds_starts[ci + 1] : a.chunk_start[ci + 1];
+          cc.gk = a.gscale[2 * ci] * a.qk_scale;
+          cc.gv = a.gscale[2 * ci + 1];
+        }
+        gk = cc.gk;
+        gv = cc.gv;
       } else {
         gk = a.qk_scale;
         gv = 1.0f;
@@ -239,8 +260,7 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnLds &L, co
 
 template <bool BF16>
 __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t attn_smem[];
-  AttnLds &L = *reinterpret_cast<AttnLds *>(attn_smem);
+  __shared__ __attribute__((aligned(16))) AttnLds L;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 31, hh = lane >> 5;
   const int h = blockIdx.y, split = blockIdx.z;
@@ -287,21 +307,31 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
     for (int v = 0; v < 16; ++v) o[i][v] = 0.0f;
 
   TileIn<BF16> fin;
+  ChunkCache cc;
+  const int32_t *lds_starts = starts_in_lds ? L.starts : nullptr;
   tile_fetch<BF16>(fin, a, h, j0, j1);
   if constexpr (!BF16) {
     if (starts_in_lds) __syncthreads();
   }
-  for (int64_t jt = j0; jt < j1; jt += kAK) {
-    tile_store<BF16>(fin, L, a, starts_in_lds);
-    __syncthreads();
+  tile_store<BF16>(fin, L.buf[0], lds_starts, cc, a);
+  __syncthreads();
+  if (j0 + kAK < j1) tile_fetch<BF16>(fin, a, h, j0 + kAK, j1);
+  int cur = 0;
+  for (int64_t jt = j0; jt < j1; jt += kAK, cur ^= 1) {
+    // decode the next tile into the other buffer (its loads were issued one
+    // tile ago), then fetch the one after it
+    if (jt + kAK < j1) {
+      tile_store<BF16>(fin, L.buf[cur ^ 1], lds_starts, cc, a);
+      if (jt + 2 * kAK < j1) tile_fetch<BF16>(fin, a, h, jt + 2 * kAK, j1);
+    }
+    const AttnTile &B = L.buf[cur];
     const int kvalid = (j1 - jt) < kAK ? (int)(j1 - jt) : kAK;
-    if (jt + kAK < j1) tile_fetch<BF16>(fin, a, h, jt + kAK, j1);
 
     // Sᵀ = K·Qᵀ: lane (query r, hh) gets keys 32kb + 8(v/4) + 4hh + v%4
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint8_t *kr = L.k + (32 * kb + r) * kKRow + 16 * hh;
+      const uint8_t *kr = B.k + (32 * kb + r) * kKRow + 16 * hh;
       f32x16 acc = {};
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
@@ -320,7 +350,7 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int key0 = 32 * kb + 8 * g4 + 4 * hh;
-        const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&L.gk[key0]);
+        const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[key0]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float tv = s[kb][4 * g4 + e] * gk4[e];
@@ -358,8 +388,8 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
       const int kb = sl >> 1, v0 = 8 * (sl & 1);
-      const f32x4 ga = *reinterpret_cast<const f32x4 *>(&L.gv[32 * kb + 8 * (v0 / 4) + 4 * hh]);
-      const f32x4 gb = *reinterpret_cast<const f32x4 *>(&L.gv[32 * kb + 8 * (v0 / 4 + 1) + 4 * hh]);
+      const f32x4 ga = *reinterpret_cast<const f32x4 *>(&B.gv[32 * kb + 8 * (v0 / 4) + 4 * hh]);
+      const f32x4 gb = *reinterpret_cast<const f32x4 *>(&B.gv[32 * kb + 8 * (v0 / 4 + 1) + 4 * hh]);
       u32x4 pk;
       pk.x = pack_bf16x2(s[kb][v0 + 0] * ga[0], s[kb][v0 + 1] * ga[1]);
       pk.y = pack_bf16x2(s[kb][v0 + 2] * ga[2], s[kb][v0 + 3] * ga[3]);
@@ -370,7 +400,7 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
     // Oᵀ += Vᵀ·Pᵀ: lane (d = 32db + r, hh) reads keys 16sl + 4hh .. +3 and 16sl + 8 + 4hh .. +3
 #pragma unroll
     for (int dbk = 0; dbk < 4; ++dbk) {
-      const uint8_t *vr = L.v + (32 * dbk + r) * kVRow + 8 * hh;
+      const uint8_t *vr = B.v + (32 * dbk + r) * kVRow + 8 * hh;
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         const u32x2 lo = *reinterpret_cast<const u32x2 *>(vr + 32 * sl);
@@ -379,6 +409,7 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
         o[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[sl], o[dbk], 0, 0, 0);
       }
     }
+    // every wave has read tile `cur` and stored the next one
     __syncthreads();
   }
 
@@ -436,13 +467,29 @@ __global__ void __launch_bounds__(kAThreads) k_attn_combine(AttnArgs a) {
   a.o[qi * a.ldo + h * kAD + d] = (uint16_t)(pack_bf16x2(val, 0.0f) & 0xFFFFu);
 }
 
+// Key splits per (query tile, head): the fewest that fill whole rounds of the
+// 512 workgroup slots of an MI355X (256 CUs, two workgroups each) to at least
+// 90 %, else the best filling; at least 8 key tiles per split, at most 32
+// splits.  Depends only on the shapes, so the workspace size does too.
 int64_t attention_splits(int64_t Tq, int64_t heads, int64_t Tk) {
+  constexpr int64_t kSlots = 512;
   const int64_t tiles = ((Tq + kAQ - 1) / kAQ) * heads;
-  int64_t want = (512 + tiles - 1) / tiles;                   // at least ~512 workgroups
-  int64_t most = Tk / (8 * kAK);                              // at least 8 key tiles per split
+  int64_t most = Tk / (8 * kAK);
   if (most > 32) most = 32;
-  if (want > most) want = most;
-  return want < 1 ? 1 : want;
+  if (most < 1) return 1;
+  int64_t best = 1;
+  double best_fill = 0.0;
+  for (int64_t n = 1; n <= most; ++n) {
+    const int64_t wgs = tiles * n;
+    const int64_t rounds = (wgs + kSlots - 1) / kSlots;
+    const double fill = (double)wgs / (double)(rounds * kSlots);
+    if (fill >= 0.9) return n;
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = n;
+    }
+  }
+  return best;
 }
 
 int64_t attention_keys_per_split(int64_t Tk, int64_t nsplit) {
@@ -452,11 +499,10 @@ int64_t attention_keys_per_split(int64_t Tk, int64_t nsplit) {
 
 hipError_t launch_attention(const AttnArgs &a, bool bf16, hipStream_t stream) {
   const dim3 grid((unsigned)((a.Tq + kAQ - 1) / kAQ), (unsigned)a.heads, (unsigned)a.nsplit);
-  const size_t lds = sizeof(AttnLds);
   if (bf16)
-    hipLaunchKernelGGL(k_attention<true>, grid, dim3(kAThreads), lds, stream, a);
+    hipLaunchKernelGGL(k_attention<true>, grid, dim3(kAThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_attention<false>, grid, dim3(kAThreads), lds, stream, a);
+    hipLaunchKernelGGL(k_attention<false>, grid, dim3(kAThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.part_o == nullptr) return e;
   const int64_t rows = a.Tq * a.heads;
