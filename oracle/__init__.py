@@ -1,4 +1,5 @@
-"""CPU oracle for the NVFP4 W4A4 linear layer and the NVFP4 KV cache.
+"""CPU oracle for the NVFP4 W4A4 linear layer, the NVFP4 KV cache, attention
+over that cache and the Hadamard-transformed weight-gradient operands.
 
 TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously correct
 definition that the HIP path is checked against.  Only the test suite, the
@@ -37,8 +38,13 @@ Parity status per function:
   nvfp4.gelu_tanh        pinned (gelu(0)=0, gelu(y)-gelu(-y)=y, large-|y| limits)
   nvfp4.KVCacheRef       pinned (byte closed form from the pages, append ≡ quantize,
                          hand-worked dequant with a non-power-of-two tensor scale)
+  nvfp4.quantize_f32     pinned (equals quantize on bf16-representable values; the
+                         binary32 steps of quantize on any binary32 input)
   attention.*            pinned (closed forms, torch's scaled_dot_product_attention
                          in float64, lossless-cache identity; see that module)
+  rht.*                  pinned (scipy's Hadamard matrix, exact rational brute force,
+                         inverse, contraction invariance, hand-worked example; see
+                         that module)
   The choices of global-scale formula, scale rounding mode, reciprocal-multiply
   order, nibble order, per-append KV scale and the binary32 error order of the
   adaptive selection are fixed by definition only
@@ -59,6 +65,7 @@ from .formats import (
 from .nvfp4 import (
     GLOBAL_DIVISOR,
     quantize,
+    quantize_f32,
     block_sq_error,
     tile_amax_2d,
     dequantize,
@@ -68,6 +75,7 @@ from .nvfp4 import (
     KVCacheRef,
 )
 from .attention import attention_ref, kv_attention_ref, range_tokens
+from .rht import hadamard, rht, rht_f64, quantize_rht
 
 __all__ = [
     "E2M1_VALUES",
@@ -81,6 +89,7 @@ __all__ = [
     "unpack_nibbles",
     "GLOBAL_DIVISOR",
     "quantize",
+    "quantize_f32",
     "block_sq_error",
     "tile_amax_2d",
     "dequantize",
@@ -91,4 +100,8 @@ __all__ = [
     "attention_ref",
     "kv_attention_ref",
     "range_tokens",
+    "hadamard",
+    "rht",
+    "rht_f64",
+    "quantize_rht",
 ]

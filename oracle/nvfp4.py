@@ -135,14 +135,23 @@ def quantize(x_bits: np.ndarray, amax=None, adaptive46=False, blocks2d=False):
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     if x_bits.ndim != 2:
         raise ValueError("x must be 2-D [M, K]")
+    return quantize_f32(bf16_bits_to_f32(x_bits), amax, adaptive46, blocks2d)
+
+
+def quantize_f32(x: np.ndarray, amax=None, adaptive46=False, blocks2d=False):
+    """The steps of ``quantize`` on binary32 values ``x`` [M, K] (any binary32,
+    not only bf16-representable ones); ``quantize`` is this function applied
+    to the bf16 inputs widened exactly to binary32."""
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2:
+        raise ValueError("x must be 2-D [M, K]")
     if adaptive46 and blocks2d:
         raise ValueError("adaptive46 and blocks2d exclude each other")
     if blocks2d and amax is not None:
         raise ValueError("blocks2d needs the whole tensor (tiles span rows)")
-    M, K = x_bits.shape
+    M, K = x.shape
     if K % BLOCK or K % 2:
         raise ValueError("K must be a multiple of 16")
-    x = bf16_bits_to_f32(x_bits)
     if not np.all(np.isfinite(x)):
         raise ValueError("inputs must be finite (R12)")
     sign = np.signbit(x).astype(np.uint8) << np.uint8(3)
