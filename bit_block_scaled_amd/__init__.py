@@ -32,7 +32,7 @@ from ._lib import (  # noqa: F401
 
 __all__ = ["quantize", "quantize_into", "gemm", "linear", "linear_noalloc", "linear_q", "KVCache", "NVFP4Error", "lib",
            "gemm_tile", "workspace", "attention_bf16", "attention_workspace_bytes", "quantize_workspace_bytes", "linear_workspace_bytes",
-           "linear_q_workspace_bytes"]
+           "linear_q_workspace_bytes", "quantize_rht", "quantize_rht_workspace_bytes", "weight_grad"]
 
 
 def _stream(device=None):
@@ -366,6 +366,49 @@ def attention_bf16(Q, K, V, scale=0.0, out=None, ws=None):
                                      _ptr(out), ldo, _ptr(ws), 0 if ws is None else ws.numel(),
                                      _stream(Q.device)))
     return out
+
+
+def quantize_rht_workspace_bytes(T: int, N: int) -> int:
+    n = C.c_size_t()
+    check(lib().nvfp4_quantize_rht_workspace(T, N, C.byref(n)))
+    return n.value
+
+
+def quantize_rht(x, sign_mask: int, codes=None, scales=None, gscale=None, ws=None):
+    """nvfp4_quantize_rht: bf16 x [T, N] (rows may be strided, features
+    contiguous) → the NVFP4 transpose of its random Hadamard transform along T:
+    (codes u8 [N, T/2], scales u8 [N, T/16], gscale f32 [1]).  ``sign_mask``
+    holds the 16 random signs (bit k set: s_k = −1); use the same mask for both
+    operands of a weight gradient."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor [T, N]")
+    T, N = x.shape
+    if not x.is_cuda or x.dtype != torch.bfloat16:
+        raise TypeError("x must be a bf16 GPU tensor")
+    if x.stride(1) != 1:
+        raise ValueError("x must have contiguous rows")
+    dev = x.device
+    if codes is None:
+        codes = torch.empty((N, T // 2), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((N, T // 16), dtype=torch.uint8, device=dev)
+    if gscale is None:
+        gscale = torch.empty((1,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty((quantize_rht_workspace_bytes(T, N),), dtype=torch.uint8, device=dev)
+    _need(codes, torch.uint8, "codes", (N, T // 2))
+    _need(scales, torch.uint8, "scales", (N, T // 16))
+    _need(gscale, torch.float32, "gscale", (1,))
+    _need(ws, torch.uint8, "ws")
+    check(lib().nvfp4_quantize_rht(_ptr(x), T, N, x.stride(0), int(sign_mask), _ptr(codes), _ptr(scales),
+                                   _ptr(gscale), _ptr(ws), ws.numel(), _stream(dev)))
+    return codes, scales, gscale
+
+
+def weight_grad(dy, x, sign_mask: int, out=None, tile=None):
+    """dW = dyᵀ·x for dy [T, O] and x [T, I] (bf16): both operands through
+    quantize_rht with the same signs, then the W4A4 GEMM → bf16 [O, I]."""
+    return gemm(*quantize_rht(dy, sign_mask), *quantize_rht(x, sign_mask), out=out, tile=tile)
 
 
 def gemm_tile(M: int, N: int, K: int) -> tuple:

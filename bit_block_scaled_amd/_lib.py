@@ -67,6 +67,8 @@ _SIGS = {
                             _p, _i64, _p, _sz, _p], C.c_int),
     "nvfp4_attention_bf16": ([_p, _i64, _i64, _p, _p, _i64, _i64, _i64, C.c_float, _p, _i64, _p, _sz, _p],
                              C.c_int),
+    "nvfp4_quantize_rht_workspace": ([_i64, _i64, C.POINTER(_sz)], C.c_int),
+    "nvfp4_quantize_rht": ([_p, _i64, _i64, _i64, C.c_uint32, _p, _p, _p, _p, _sz, _p], C.c_int),
     "nvfp4_testing_set_quantize_wait": ([C.c_uint64], C.c_uint64),
     "nvfp4_testing_set_launch_events": ([C.POINTER(C.c_void_p), C.c_int], C.c_int),
     "nvfp4_strerror": ([C.c_int], C.c_char_p),

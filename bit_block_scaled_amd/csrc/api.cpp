@@ -463,6 +463,34 @@ static int run_attention(nvfp4::AttnArgs &a, bool bf16, float scale, void *ws, s
   return launched(nvfp4::launch_attention(a, bf16, st), st, who);
 }
 
+int nvfp4_quantize_rht_workspace(int64_t T, int64_t N, size_t *bytes) {
+  if (bytes == nullptr) return fail(NVFP4_EINVAL, "bytes is NULL");
+  if (T < 32 || T % 32) return fail(NVFP4_EINVAL, "quantize_rht_workspace: T must be a positive multiple of 32");
+  if (N < 1 || N > kMaxElements / T) return fail(NVFP4_EINVAL, "quantize_rht_workspace: bad N");
+  *bytes = 4 * size_t(nvfp4::kRhtMaxParts);
+  return NVFP4_OK;
+}
+
+int nvfp4_quantize_rht(const uint16_t *x, int64_t T, int64_t N, int64_t ldx, uint32_t sign_mask,
+                       uint8_t *codes, uint8_t *scales, float *gscale, void *ws, size_t ws_bytes,
+                       void *stream) {
+  int s;
+  size_t need = 0;
+  if ((s = nvfp4_quantize_rht_workspace(T, N, &need))) return s;
+  if (ldx < N || ldx % 8) return fail(NVFP4_EINVAL, "quantize_rht: ldx must be >= N and a multiple of 8");
+  if (ldx > kMaxElements / T) return fail(NVFP4_EINVAL, "quantize_rht: ldx*T too large");
+  if (sign_mask >> 16) return fail(NVFP4_EINVAL, "quantize_rht: sign_mask has 16 bits");
+  if ((s = check_ptr(x, "x"))) return s;
+  if ((s = check_ptr(codes, "codes"))) return s;
+  if ((s = check_ptr(scales, "scales"))) return s;
+  if ((s = check_ptr(gscale, "gscale", 4))) return s;
+  if (ws == nullptr || ws_bytes < need) return fail(NVFP4_EWORKSPACE, "quantize_rht: workspace too small");
+  if ((s = check_ptr(ws, "ws", 4))) return s;
+  nvfp4::RhtArgs a{x, T, N, ldx, sign_mask, codes, scales, gscale, static_cast<uint32_t *>(ws)};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(nvfp4::launch_quantize_rht(a, st), st, "quantize_rht");
+}
+
 int nvfp4_kv_attention_workspace(int64_t Tq, int64_t heads, int64_t Tk, size_t *bytes) {
   if (bytes == nullptr) return fail(NVFP4_EINVAL, "bytes is NULL");
   if (Tq < 1 || heads < 1 || Tk < 1) return fail(NVFP4_EINVAL, "kv_attention_workspace: Tq, heads and Tk must be >= 1");

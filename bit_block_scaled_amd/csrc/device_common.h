@@ -77,6 +77,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, 
   return r;
 }
 
+// Per-tensor constants of the block-scale arithmetic.  Both divisions of a
+// block are done with FMA refinements that return the correctly rounded
+// binary32 result:
+//   s_raw = fl(a / 6g): a and 6g are first scaled by the same power of two
+//     (exact) so 6g lies in [1, 2); then q0 = a·y with y = fl(1/6g), the
+//     residual a − q0·6g (exact by FMA) and q0 + residual·y rounded once give
+//     the correctly rounded quotient (Markstein's theorem: y is the correctly
+//     rounded reciprocal and q0 lies within one ulp of the quotient; for bf16
+//     block maxima an exhaustive CPU check finds no E4M3 byte that differs);
+//   r = fl(1/d): one Newton step y0 + y0·(1 − d·y0) from the hardware
+//     reciprocal (within 1 ulp) rounds correctly for every binary32
+//     significand (checked exhaustively on the CPU).
+// The block amax maps to `target` (6, or 4 for the second candidate of the
+// adaptive selection), i.e. the divisor is fl(target·g).
+struct BlockScaler {
+  float g, sc, bs, y;
+  __device__ __forceinline__ BlockScaler(float g_, float target) : g(g_) {
+    const float div = target * g;                                 // fl(target·g)
+    sc = __uint_as_float((254u - ((__float_as_uint(div) >> 23) & 0xFFu)) << 23);   // 2^-e(div)
+    bs = div * sc;
+    y = 1.0f / bs;
+  }
+  // E4M3 scale byte of a block whose largest magnitude is a (binary32, >= 0).
+  __device__ __forceinline__ uint32_t scale_byte_of(float a) const {
+    const float as = a * sc;
+    const float q0 = as * y;
+    const float res = __builtin_fmaf(-q0, bs, as);
+    return e4m3_encode_rne_sat(__builtin_fmaf(res, y, q0));       // fl(a / div) → E4M3
+  }
+  // The same for a largest magnitude given as its bf16 pattern bm.
+  __device__ __forceinline__ uint32_t scale_byte(uint32_t bm) const {
+    return scale_byte_of(bf16_bits_to_f32(bm));
+  }
+  // fl(1 / fl(S·g)), 0 for S == 0.
+  __device__ __forceinline__ float recip(uint32_t S) const {
+    const float d = e4m3_decode(S) * g;                           // fl(S·g)
+    const float y0 = __builtin_amdgcn_rcpf(d);
+    const float e = __builtin_fmaf(-d, y0, 1.0f);
+    const float r = __builtin_fmaf(e, y0, y0);
+    return S == 0 ? 0.0f : r;
+  }
+};
+
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {

@@ -134,4 +134,21 @@ int64_t attention_splits(int64_t Tq, int64_t heads, int64_t Tk);
 int64_t attention_keys_per_split(int64_t Tk, int64_t nsplit);
 hipError_t launch_attention(const AttnArgs &a, bool bf16, hipStream_t stream);
 
+// Weight-gradient operand: x [T, N] bf16 (token t at x + t·ld, T a multiple of
+// 32, ld a multiple of 8), transformed per group of 16 tokens by
+// H16·diag(s)/4 (s_k = −1 where bit k of sign_mask is set) and quantised as
+// its transpose [N, T]: codes [N, T/2], scales [N, T/16], *gscale.  partials
+// holds kRhtMaxParts words, written before they are read (no initialisation).
+constexpr int kRhtMaxParts = 2048;
+struct RhtArgs {
+  const uint16_t *x;
+  int64_t T, N, ld;
+  uint32_t sign_mask;
+  uint8_t *codes, *scales;
+  float *gscale;
+  uint32_t *partials;
+};
+int64_t rht_tiles(int64_t T, int64_t N);
+hipError_t launch_quantize_rht(const RhtArgs &a, hipStream_t stream);
+
 }  // namespace nvfp4

@@ -148,44 +148,6 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t old, uint32_t w, float r) 
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, x0 * r, x1 * r, 1.0f, SEL);
 }
 
-// Per-tensor constants of the block-scale arithmetic.  Both divisions of a
-// block are done with FMA refinements that return the correctly rounded
-// binary32 result:
-//   s_raw = fl(a / 6g): a and 6g are first scaled by the same power of two
-//     (exact) so 6g lies in [1, 2); then q0 = a·y with y = fl(1/6g), the
-//     residual a − q0·6g (exact by FMA) and q0 + residual·y rounded once give
-//     the correctly rounded quotient (Markstein's theorem; an exhaustive CPU
-//     check over the input domain finds no E4M3 byte that differs);
-//   r = fl(1/d): one Newton step y0 + y0·(1 − d·y0) from the hardware
-//     reciprocal (within 1 ulp) rounds correctly for every binary32
-//     significand (checked exhaustively on the CPU).
-// The block amax maps to `target` (6, or 4 for the second candidate of the
-// adaptive selection), i.e. the divisor is fl(target·g).
-struct BlockScaler {
-  float g, sc, bs, y;
-  __device__ __forceinline__ BlockScaler(float g_, float target) : g(g_) {
-    const float div = target * g;                                 // fl(target·g)
-    sc = __uint_as_float((254u - ((__float_as_uint(div) >> 23) & 0xFFu)) << 23);   // 2^-e(div)
-    bs = div * sc;
-    y = 1.0f / bs;
-  }
-  // E4M3 scale byte of a block whose largest magnitude has bf16 pattern bm.
-  __device__ __forceinline__ uint32_t scale_byte(uint32_t bm) const {
-    const float as = bf16_bits_to_f32(bm) * sc;
-    const float q0 = as * y;
-    const float res = __builtin_fmaf(-q0, bs, as);
-    return e4m3_encode_rne_sat(__builtin_fmaf(res, y, q0));       // fl(a / div) → E4M3
-  }
-  // fl(1 / fl(S·g)), 0 for S == 0.
-  __device__ __forceinline__ float recip(uint32_t S) const {
-    const float d = e4m3_decode(S) * g;                           // fl(S·g)
-    const float y0 = __builtin_amdgcn_rcpf(d);
-    const float e = __builtin_fmaf(-d, y0, 1.0f);
-    const float r = __builtin_fmaf(e, y0, y0);
-    return S == 0 ? 0.0f : r;
-  }
-};
-
 // E2M1 codes of one 16-element block (8 bf16 pairs) scaled by r: element 2j
 // in the low nibble of byte j, elements 0..7 in lo, 8..15 in hi.
 __device__ __forceinline__ void encode_codes(const uint32_t (&w)[8], float r, uint32_t &lo,

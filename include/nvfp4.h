@@ -332,6 +332,44 @@ int nvfp4_attention_bf16(const uint16_t *Q, int64_t Tq, int64_t ldq, const uint1
                          const uint16_t *V, int64_t Tk, int64_t ldkv, int64_t heads, float scale,
                          uint16_t *O, int64_t ldo, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Bytes of scratch nvfp4_quantize_rht needs (8192: one partial maximum per
+ * workgroup, written before it is read, so the scratch needs no
+ * initialisation).  Fails like nvfp4_quantize_rht on a bad shape.
+ */
+int nvfp4_quantize_rht_workspace(int64_t T, int64_t N, size_t *bytes);
+
+/*
+ * Weight-gradient operand with a random Hadamard transform: transforms x along
+ * its token axis and NVFP4-quantises the transpose, so two such operands feed
+ * nvfp4_gemm for dW = dyᵀ·x (M = features of dy, N = features of x, K = T).
+ * Source: 二、方法 / NVFP4 训练的工程细节 (a random Hadamard transform precedes
+ * the quantisation of the weight-gradient GEMM's operands; gradients take 1-D
+ * block scales) and 二、方法 / NVFP4 量化格式.
+ *
+ *   x          bf16 [T, N], token t at x + t·ldx; 16-byte aligned, ldx >= N,
+ *              ldx % 8 == 0 (rows 16-byte aligned)
+ *   sign_mask  the 16 random signs s_k (bit k set: s_k = −1), drawn by the
+ *              caller; pass the same mask for both operands of one product
+ *   codes      out: uint8 [N, T/2]  E2M1 codes of the transpose, two per byte,
+ *              16-byte aligned (so are scales)
+ *   scales     out: uint8 [N, T/16] E4M3 block scales (16 tokens per block)
+ *   gscale     out: float [1]       FP32 tensor scale g
+ *   ws         scratch of nvfp4_quantize_rht_workspace(T, N) bytes
+ *
+ * Arithmetic: per group of 16 consecutive tokens (from token 0) and feature n,
+ * y = H16·diag(s)·x/4 with Sylvester's H16 (H[i,k] = (−1)^popcount(i&k));
+ * the sums are formed exactly (binary64; exact while a group spans less than
+ * 2^41 in magnitude) and rounded once to binary32, an exact zero as +0; then
+ * the steps of nvfp4_quantize on yᵀ (A = max|y|, g = A/2688, …).  Requires
+ * T >= 32, T % 32 == 0 (append zero tokens otherwise: they add nothing to the
+ * weight gradient), N >= 1, |x| small enough that y stays finite (below 2^124).
+ * Two launches on `stream`.
+ */
+int nvfp4_quantize_rht(const uint16_t *x, int64_t T, int64_t N, int64_t ldx, uint32_t sign_mask,
+                       uint8_t *codes, uint8_t *scales, float *gscale,
+                       void *ws, size_t ws_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage). */
 const char *nvfp4_strerror(int status);
 

@@ -23,7 +23,9 @@ Readings taken where the pages are silent:
       same R on every group and on both operands, so that
       Σ_t (R·dy)[t, o] (R·x)[t, i] = Σ_t dy[t, o] x[t, i] (R is orthogonal);
   R31 the transformed values are exact sums of ±bf16 inputs divided by 4,
-      rounded once to binary32 (nearest-even); the tensor amax and every
+      rounded once to binary32 (nearest-even), an exactly zero value as +0
+      (the sign of an exact zero is an artefact of the summation order and of
+      sign flips on zero inputs, so it is fixed); the tensor amax and every
       quantisation decision then follow the binary32 steps of the NVFP4
       quantiser on those values.  (The exact sum of a group is representable
       in binary64 whenever its 16 inputs span less than 2^41 in magnitude,
@@ -98,7 +100,8 @@ def rht(x_bits: np.ndarray, sign_mask: int) -> np.ndarray:
     low = np.where(a > 0, a, np.inf).min(axis=1)
     if np.any((top > 0) & (top >= low * 2.0 ** 41)):
         raise ValueError("a group spans 2^41 or more; its binary64 sum may round (R31)")
-    return rht_f64(x, sign_mask).astype(np.float32)     # exact in binary64, one rounding
+    y = rht_f64(x, sign_mask) + 0.0                      # exact in binary64; −0 → +0
+    return y.astype(np.float32)                           # one rounding
 
 
 def quantize_rht(x_bits: np.ndarray, sign_mask: int):

@@ -225,3 +225,28 @@ def test_launch_event_hook_rejects(L):
     assert L.nvfp4_testing_set_launch_events(None, 2) == EINVAL
     assert L.nvfp4_testing_set_launch_events(None, -1) == EINVAL
     assert L.nvfp4_testing_set_launch_events(None, 0) == 0
+
+
+def test_quantize_rht_rejects(L):
+    n = C.c_size_t()
+    assert L.nvfp4_quantize_rht_workspace(8192, 14336, C.byref(n)) == 0 and n.value >= 4
+    assert L.nvfp4_quantize_rht_workspace(48, 64, C.byref(n)) == EINVAL            # T % 32
+    assert L.nvfp4_quantize_rht_workspace(64, 0, C.byref(n)) == EINVAL
+    f = L.nvfp4_quantize_rht
+    ok = (FAKE, 64, 40, 40, 0x1234, FAKE, FAKE, FAKE, FAKE, 1 << 20, None)
+    def call(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[["x", "T", "N", "ldx", "mask", "codes", "scales", "g", "ws", "wsb", "st"].index(k)] = v
+        return f(*a)
+    assert call(T=48) == EINVAL                  # not a multiple of 32
+    assert call(ldx=36) == EINVAL                # below N
+    assert call(ldx=44) == EINVAL                # not a multiple of 8
+    assert call(mask=1 << 16) == EINVAL          # 17-bit sign mask
+    assert call(x=MIS) == EINVAL
+    assert call(codes=None) == EINVAL
+    assert call(scales=MIS) == EINVAL
+    assert call(g=FAKE + 2) == EINVAL
+    assert call(wsb=16) == EWS
+    assert call(ws=None) == EWS
+    assert b"quantize_rht" in L.nvfp4_last_error()

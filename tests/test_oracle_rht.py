@@ -146,6 +146,23 @@ def test_heavy_tails_become_closer_to_normal():
     assert np.isclose(np.sum(y * y), np.sum(xf * xf), rtol=1e-6)   # energy kept (orthogonal)
 
 
+def test_exact_zeros_are_positive():
+    # zero groups (+0 and -0 inputs) under a mask that flips every sign, and a
+    # group whose transform cancels exactly: every zero output is +0 and
+    # encodes as code 0, not 0x8
+    x = np.zeros((32, 3), dtype=np.float32)
+    x[:16, 1] = -0.0
+    x[16:32, 2] = np.r_[1.0, 1.0, np.zeros(14)]           # H·x has zeros at odd i
+    xb = _bits(x)
+    y = oracle.rht(xb, 0xFFFF)
+    zero = y == 0
+    assert zero.sum() > 60 and not np.signbit(y[zero]).any()
+    codes, scales, _ = oracle.quantize_rht(xb, 0xFFFF)
+    assert not codes[:2].any() and not scales[:2].any()
+    nib = oracle.unpack_nibbles(codes[2:3])[0, 16:32]
+    assert np.array_equal(nib[1::2], np.zeros(8, np.uint8))
+
+
 def test_rejects_bad_inputs():
     with pytest.raises(ValueError):
         oracle.quantize_rht(np.zeros((48, 4), dtype=np.uint16), 0)      # T not a multiple of 32

@@ -19,6 +19,10 @@ the DiT, NVFP4 KV cache; the 5B DiT has 24 heads of 128 = 3072 channels):
   kv     K, V [65536, 24, 128] ~ N(0,1) × a per-head factor U(0.5, 4)
          (24 draws for K, then 24 for V, constant over tokens), appended in
          74 chunks of 880 tokens and one of 416;  seed 4
+  wgrad  weight gradient of the FFN up-projection over T = 8192 tokens:
+         dY [T, 14336] ~ N(0, 10^-3) × a per-token factor exp(N(0, 0.5²)),
+         X [T, 3072] ~ N(0,1) with 0.1 % ×50; then the 16 random signs of the
+         Hadamard transform as a 16-bit mask;  seed 5
 
 σ in N(0, σ) is the standard deviation.  Draw order inside a workload: X, then
 W (then W_down), then bias, then outlier positions.
@@ -138,6 +142,25 @@ def kv(seed: int = 4, tokens: int = KV_TOKENS, heads: int = HEADS, head_dim: int
     k = _normal(rng, (tokens, heads, head_dim)) * fk[None, :, None]
     v = _normal(rng, (tokens, heads, head_dim)) * fv[None, :, None]
     return to_bf16_bits(k), to_bf16_bits(v), kv_chunk_sizes(tokens)
+
+
+@dataclass
+class WgradWorkload:
+    name: str
+    seed: int
+    dy: np.ndarray                # bf16 bits [T, O]
+    x: np.ndarray                 # bf16 bits [T, I]
+    sign_mask: int
+
+
+def wgrad(seed: int = 5, T: int = 8192, O: int = 14336, I: int = 3072) -> WgradWorkload:
+    rng = np.random.default_rng(seed)
+    tok = np.exp(rng.standard_normal((T, 1)) * 0.5).astype(np.float32)
+    dy = _normal(rng, (T, O), 1e-3) * tok
+    x = _outliers(rng, _normal(rng, (T, I)))
+    mask = int(rng.integers(0, 1 << 16))
+    return WgradWorkload(f"FFN up weight gradient dW [{O}, {I}] = dYᵀ·X over {T} tokens", seed,
+                         to_bf16_bits(dy), to_bf16_bits(x), mask)
 
 
 def random_matrix(seed: int, M: int, K: int, sigma: float = 1.0, outliers: bool = False):
