@@ -22,13 +22,15 @@ gives the per-kernel breakdown and the dominant kernel's roofline (the up
 GEMM).  Further entries in `kernels` time the other configurations' kernels
 (QKV and long-context GEMMs and quantisers, the 65536-token KV append
 sequence and its read-back, attention of an 880-token query chunk over that
-cache read in NVFP4 against the same kernel on bf16 K/V, a 1 GiB device
-copy) with p10/p50/p90 over repetitions; the HBM-bound ones after a 1 GiB
-cache flush ("cold").
+cache read in NVFP4 against the same kernel on bf16 K/V, the FFN up
+projection's weight gradient with Hadamard-transformed operands, a 1 GiB
+device copy) with p10/p50/p90 over repetitions; the HBM-bound ones after a
+1 GiB cache flush ("cold").
 `cpu_baseline` is the CPU oracle on a bounded sample of the FFN step.
 
 Other modes: --copy-only (1 GiB copy, for rocprofv3 counter calibration),
---gemm-clock (QKV GEMM on benchmark vs constant operands).
+--gemm-clock (QKV GEMM on benchmark vs constant operands), --wgrad-only (the
+weight-gradient configuration alone).
 """
 
 from __future__ import annotations
@@ -80,6 +82,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
     ap.add_argument("--copy-only", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--wgrad-only", action="store_true",
+                    help="run only the FFN weight-gradient configuration (Hadamard-transformed operands and "
+                         "their GEMM) and print its timings (for rocprofv3)")
     ap.add_argument("--gemm-clock", action="store_true",
                     help="run only the QKV GEMM, 20 launches on the benchmark's operands, then 20 on "
                          "constant-byte operands (for rocprofv3 --pmc GRBM_GUI_ACTIVE)")
@@ -229,6 +234,11 @@ def main():
 
     if a.gemm_clock:
         gemm_clock(a, nv, torch, np, workloads, dev, up)
+        return
+    if a.wgrad_only:
+        kernels = {}
+        wgrad_leg(kernels, nv, torch, np, workloads, dev, up, CacheFlush(torch, dev))
+        print(json.dumps({"kernels": kernels}))
         return
 
     # ------------------------------------------------------------------ FFN step
@@ -522,7 +532,44 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
         del ws_a
     del cache, ko, vo, qa, oa
     torch.cuda.empty_cache()
+
+    wgrad_leg(kernels, nv, torch, np, workloads, dev, up, flush)
     return round(float(copy_gbs), 1)
+
+
+def wgrad_leg(kernels, nv, torch, np, workloads, dev, up, flush):
+    """The weight-gradient configuration (added to `kernels`)."""
+    # weight gradient of the FFN up-projection over 8192 tokens: dY and X each
+    # through the random Hadamard transform and the NVFP4 quantisation of
+    # their transposes (cold; two launches that read the operand twice, since
+    # the tensor amax of the transform precedes every block scale), then the
+    # W4A4 GEMM dW = dYᵀ·X
+    log("extras: FFN weight gradient with the Hadamard transform")
+    wg = workloads.wgrad()
+    T = wg.x.shape[0]
+    ops = {"dy": up(wg.dy), "x": up(wg.x)}
+    mask = wg.sign_mask
+    del wg
+    qops = {}
+    for k, xt in ops.items():
+        N = xt.shape[1]
+        c = torch.empty((N, T // 2), dtype=torch.uint8, device=dev)
+        s_ = torch.empty((N, T // 16), dtype=torch.uint8, device=dev)
+        g = torch.empty((1,), dtype=torch.float32, device=dev)
+        ws_r = torch.empty((nv.quantize_rht_workspace_bytes(T, N),), dtype=torch.uint8, device=dev)
+        t = time_us(torch, lambda xt=xt, c=c, s_=s_, g=g, ws_r=ws_r: nv.quantize_rht(xt, mask, c, s_, g, ws_r),
+                    30, 5, flush)
+        kernels[f"wgrad_quantize_rht_{k}_cold"] = {
+            "shape": [T, N], "us": pct(t), "hbm_bytes_moved": T * N * (2 * 2 + 0.5 + 1 / 16),
+            "roofline": roof_hbm(T * N * Q_BYTES_PER_ELEM + 4, float(np.median(t)))}
+        qops[k] = (c, s_, g)
+    O, I = ops["dy"].shape[1], ops["x"].shape[1]
+    dW = torch.empty((O, I), dtype=torch.bfloat16, device=dev)
+    t = time_us(torch, lambda: nv.gemm(*qops["dy"], *qops["x"], out=dW), 30, 10)
+    kernels["wgrad_gemm"] = {"shape": [O, I, T], "tile": list(nv.gemm_tile(O, I, T)), "us": pct(t),
+                             "roofline": roof_gemm(2.0 * O * I * T, float(np.median(t)))}
+    del ops, qops, dW
+    torch.cuda.empty_cache()
 
 
 def gemm_clock(a, nv, torch, np, workloads, dev, up):

@@ -16,18 +16,22 @@
 // Arithmetic.  The butterflies run in binary64, where a sum of 16 bf16 values
 // is exact unless the group spans 2^41 or more in magnitude; each output is
 // rounded once to binary32 (an exact zero as +0: a sign-flipped zero input
-// would otherwise leave −0 in the sums).  The factor 1/4 is a power of two, so the kernel
-// keeps u = fl32(4y) and applies 1/4 exactly where y enters: the block amax
+// would otherwise leave −0 in the sums).  The factor 1/4 is a power of two,
+// so the kernel keeps u = fl32(4y) and applies 1/4 exactly where y enters: the block amax
 // (a = max|u| / 4) and the reciprocal (u·(r/4) rounds like y·r).  The tensor
 // amax, the E4M3 block scales and the E2M1 codes then follow the binary32
 // steps of the NVFP4 quantiser.
 //
-// Layout of the work.  A workgroup pass covers 256 tokens × 128 features with
-// 256 threads; thread (group = tid/16, c = tid%16) holds the 16 tokens of one
-// group for 8 consecutive features (16 loads of 16 bytes: one wave reads four
-// 256-byte row segments per load).  Each of its 8 columns is exactly one NVFP4
-// block of the transpose, so block maxima need no exchange between threads.
-// The 128 rows × 128 code bytes and 128 × 16 scale bytes of the transpose are
+// Layout of the work.  A workgroup pass covers 256 tokens × 16·kFeat features
+// with 256 threads; thread (group = tid/16, c = tid%16) holds the 16 tokens of
+// one group for kFeat consecutive features (16 loads of 2·kFeat bytes: one
+// wave reads four row segments of 32·kFeat bytes per load).  kFeat = 4 keeps
+// the encode kernel at three waves per SIMD (8 features need two, and lose
+// 7 % on the 8192 × 14336 operand; prefetching the next tile into registers
+// costs more occupancy than it hides).  Each of its
+// columns is exactly one NVFP4 block of the transpose, so block maxima need no
+// exchange between threads.  The code bytes (128 per feature) and scale bytes
+// (16 per feature) of the transpose are
 // staged in LDS and written as whole row segments.  Two launches: the first
 // writes one partial amax per workgroup; the second folds them into g, then
 // transforms again and encodes, visiting the tiles in reverse order so that
@@ -39,9 +43,12 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kFeat = 4;                     // features per thread (one 8-byte load per token)
+constexpr int kWords = kFeat / 2;            // bf16 pairs per token and thread
 constexpr int kTileT = 256;                  // tokens per workgroup pass
-constexpr int kTileN = 128;                  // features per workgroup pass
-constexpr int kCodeStride = kTileN + 16;     // LDS row of code bytes, 16-byte aligned
+constexpr int kTileN = 16 * kFeat;           // features per workgroup pass
+constexpr int kCodeStride = kTileT / 2 + 16; // LDS row of code bytes, 16-byte aligned
+typedef __attribute__((ext_vector_type(kWords))) uint32_t load_t;
 
 struct Tile {
   int64_t t0, n0;
@@ -52,35 +59,33 @@ __device__ __forceinline__ Tile tile_of(const RhtArgs &a, int64_t tile) {
   return Tile{(tile / ntn) * kTileT, (tile % ntn) * kTileN};
 }
 
-// The 16 tokens of this thread's group × its 8 features, as bf16 pairs
+// The 16 tokens of this thread's group × its kFeat features, as bf16 pairs
 // (w[i][d] holds features 2d, 2d+1 of token i), each row's sign applied.
 // Tokens past T and features past N read as 0.
-__device__ __forceinline__ void load_group(const RhtArgs &a, const Tile &tl, uint32_t (&w)[16][4]) {
+__device__ __forceinline__ void load_group(const RhtArgs &a, const Tile &tl, uint32_t (&w)[16][kWords]) {
   const int grp = threadIdx.x >> 4, c = threadIdx.x & 15;
-  const int64_t t = tl.t0 + 16 * grp, n = tl.n0 + 8 * c;
+  const int64_t t = tl.t0 + 16 * grp, n = tl.n0 + kFeat * c;
   if (t >= a.T || n >= a.N) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) w[i][d] = 0u;
+      for (int d = 0; d < kWords; ++d) w[i][d] = 0u;
     return;
   }
   const uint16_t *p = a.x + t * a.ld + n;
-  if (n + 8 <= a.N) {
+  if (n + kFeat <= a.N) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(p + i * a.ld);
-      w[i][0] = v.x;
-      w[i][1] = v.y;
-      w[i][2] = v.z;
-      w[i][3] = v.w;
+      const load_t v = *reinterpret_cast<const load_t *>(p + i * a.ld);
+#pragma unroll
+      for (int d = 0; d < kWords; ++d) w[i][d] = v[d];
     }
   } else {
     const int valid = (int)(a.N - n);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+      for (int d = 0; d < kWords; ++d) {
         const uint32_t lo = (2 * d < valid) ? p[i * a.ld + 2 * d] : 0u;
         const uint32_t hi = (2 * d + 1 < valid) ? p[i * a.ld + 2 * d + 1] : 0u;
         w[i][d] = lo | (hi << 16);
@@ -91,7 +96,7 @@ __device__ __forceinline__ void load_group(const RhtArgs &a, const Tile &tl, uin
   for (int i = 0; i < 16; ++i) {
     const uint32_t flip = ((a.sign_mask >> i) & 1u) ? 0x80008000u : 0u;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) w[i][d] ^= flip;
+    for (int d = 0; d < kWords; ++d) w[i][d] ^= flip;
   }
 }
 
@@ -109,8 +114,8 @@ __device__ __forceinline__ void fwht16(double (&v)[16]) {
       }
 }
 
-// Feature e (0..7) of the thread's group, signed, as binary64, transformed.
-__device__ __forceinline__ void column(const uint32_t (&w)[16][4], int e, double (&v)[16]) {
+// Feature e of the thread's group, signed, as binary64, transformed.
+__device__ __forceinline__ void column(const uint32_t (&w)[16][kWords], int e, double (&v)[16]) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint32_t d = w[i][e >> 1];
@@ -122,10 +127,10 @@ __device__ __forceinline__ void column(const uint32_t (&w)[16][4], int e, double
 __global__ void __launch_bounds__(kThreads) k_rht_amax(RhtArgs a, int64_t ntiles) {
   double m = 0.0;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    uint32_t w[16][4];
+    uint32_t w[16][kWords];
     load_group(a, tile_of(a, tile), w);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < kFeat; ++e) {
       double v[16];
       column(w, e, v);
 #pragma unroll
@@ -178,10 +183,10 @@ __global__ void __launch_bounds__(kThreads) k_rht_encode(RhtArgs a, int64_t ntil
   const int64_t half_t = a.T / 2, sixteenth_t = a.T / 16;
   for (int64_t tile = ntiles - 1 - blockIdx.x; tile >= 0; tile -= gridDim.x) {
     const Tile tl = tile_of(a, tile);
-    uint32_t w[16][4];
+    uint32_t w[16][kWords];
     load_group(a, tl, w);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < kFeat; ++e) {
       double v[16];
       column(w, e, v);
       float u[16];
@@ -202,15 +207,15 @@ __global__ void __launch_bounds__(kThreads) k_rht_encode(RhtArgs a, int64_t ntil
       hi = cvt_pair_f32<1>(hi, u[10], u[11], r);
       hi = cvt_pair_f32<2>(hi, u[12], u[13], r);
       hi = cvt_pair_f32<3>(hi, u[14], u[15], r);
-      const int row = 8 * c + e;                               // feature within the tile
+      const int row = kFeat * c + e;                           // feature within the tile
       *reinterpret_cast<u32x2 *>(cd + row * kCodeStride + 8 * grp) = u32x2{lo, hi};
       sc[row * 16 + grp] = (uint8_t)S;
     }
     __syncthreads();
-    // 128 rows × 8 chunks of 16 code bytes (32 tokens each); T is a multiple
-    // of 32, so a chunk is wholly inside or outside the tensor
+    // kTileN rows × 8 chunks of 16 code bytes (32 tokens each); T is a
+    // multiple of 32, so a chunk is wholly inside or outside the tensor
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kTileN * 8 / kThreads; ++it) {
       const int q = threadIdx.x + kThreads * it;
       const int row = q >> 3, part = q & 7;
       const int64_t n = tl.n0 + row;
@@ -219,9 +224,9 @@ __global__ void __launch_bounds__(kThreads) k_rht_encode(RhtArgs a, int64_t ntil
         *reinterpret_cast<u32x4 *>(a.codes + n * half_t + tl.t0 / 2 + 16 * part) = v;
       }
     }
-    // 128 rows × 8 pairs of scale bytes (32 tokens each)
+    // kTileN rows × 8 pairs of scale bytes (32 tokens each)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < kTileN * 8 / kThreads; ++it) {
       const int q = threadIdx.x + kThreads * it;
       const int row = q >> 3, pr = q & 7;
       const int64_t n = tl.n0 + row;
