@@ -520,8 +520,11 @@ int nvfp4_kv_attention(const nvfp4_kv_cache *c, const uint16_t *Q, int64_t Tq, i
     a.range_len[i] = hi - lo;
     Tk += hi - lo;
   }
+  if (c->n_tokens >= (int64_t(1) << 24) || c->n_tokens * c->heads * 128 > (int64_t(1) << 31))
+    return fail(NVFP4_EINVAL, "kv_attention: the cache must hold fewer than 2^24 tokens and at most 2^31 elements per tensor");
   a.n_ranges = n_ranges;
   a.Tk = Tk;
+  a.kv_tokens = c->n_tokens;
   a.q = Q;
   a.ldq = ldq;
   a.o = O;
@@ -545,7 +548,8 @@ int nvfp4_attention_bf16(const uint16_t *Q, int64_t Tq, int64_t ldq, const uint1
   if ((s = check_attn_common(Q, Tq, ldq, heads, O, ldo, scale, "attention_bf16"))) return s;
   if (Tk < 1) return fail(NVFP4_EINVAL, "attention_bf16: Tk must be >= 1");
   if (ldkv < heads * 128 || ldkv % 8) return fail(NVFP4_EINVAL, "attention_bf16: ldkv must be >= heads*128 and a multiple of 8");
-  if (Tk > kMaxElements / ldkv) return fail(NVFP4_EINVAL, "attention_bf16: Tk too large");
+  if (Tk >= (int64_t(1) << 24) || Tk * ldkv > (int64_t(1) << 30))
+    return fail(NVFP4_EINVAL, "attention_bf16: Tk must be below 2^24 and Tk*ldkv at most 2^30 (K and V below 2^31 bytes)");
   if ((s = check_ptr(K, "K"))) return s;
   if ((s = check_ptr(V, "V"))) return s;
   nvfp4::AttnArgs a{};
@@ -553,6 +557,7 @@ int nvfp4_attention_bf16(const uint16_t *Q, int64_t Tq, int64_t ldq, const uint1
   a.range_len[0] = Tk;
   a.n_ranges = 1;
   a.Tk = Tk;
+  a.kv_tokens = Tk;
   a.q = Q;
   a.ldq = ldq;
   a.o = O;

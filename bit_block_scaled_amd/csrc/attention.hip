@@ -46,17 +46,19 @@ constexpr int kAThreads = 256;
 constexpr int kKRow = kAD * 2 + 16;       // LDS bytes per K row (272)
 constexpr int kVRow = kAK * 2 + 8;        // LDS bytes per Vᵀ row (136)
 constexpr int kAttnLdsStarts = 2048;      // chunk starts kept in LDS (as int32)
+constexpr float kLazy = 8.0f;             // log2 headroom of the softmax reference
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
 // One decoded key tile.  The workgroup keeps two: it decodes tile i+1 into
 // one while its waves read tile i from the other, so one barrier per tile
 // orders both.
-struct AttnTile {
+struct alignas(16) AttnTile {     // 16-byte multiple: both buffers keep 16-byte rows aligned
   uint8_t k[kAK * kKRow];
   uint8_t v[kAD * kVRow];
-  float gk[kAK], gv[kAK];
+  float gk[kAK], gv[kAK];     // per key: g_K·scale·log2(e) and g_V (0 past the keys)
 };
+static_assert(sizeof(AttnTile) % 16 == 0, "tile buffers must stay 16-byte aligned");
 struct AttnLds {
   AttnTile buf[2];
   int32_t starts[kAttnLdsStarts];
@@ -66,7 +68,7 @@ struct AttnLds {
 // its factors: consecutive tiles move each slot's token forward by 64, so the
 // append only has to be searched again when a token leaves [lo, hi).
 struct ChunkCache {
-  int64_t lo = 0, hi = 0;
+  int32_t lo = 0, hi = 0;
   float gk = 0.0f, gv = 0.0f;
 };
 
@@ -106,62 +108,84 @@ struct TileIn<false> {
   uint32_t kscale;          // two scale bytes
   u32x2 vcode[2];
   uint32_t vscale[2];
-  int64_t tok;
+  int32_t tok;
 };
 template <>
 struct TileIn<true> {
   u32x4 kraw[4];            // 32 bf16
   u32x4 vraw[2][2];         // 16 bf16 per key
-  int64_t tok;
+  int32_t tok;
 };
 
+// Token of the tile's first key when all its keys jt .. min(jt + 64, j1) − 1
+// lie in one range (the usual case), else −1.  Depends only on kernel
+// arguments and the tile: uniform, so it runs on the scalar unit.
+__device__ __forceinline__ int64_t tile_run_token(const AttnArgs &a, int64_t jt, int64_t j1) {
+  const int64_t n = (jt + kAK < j1 ? jt + kAK : j1) - jt;
+  int64_t j = jt, base = -1;
+  bool found = false;
+#pragma unroll
+  for (int r = 0; r < kAttnMaxRanges; ++r) {
+    if (r < a.n_ranges && !found) {
+      if (j < a.range_len[r]) {
+        found = true;
+        base = (j + n <= a.range_len[r]) ? a.range_lo[r] + j : -1;
+      }
+      j -= a.range_len[r];
+    }
+  }
+  return base;
+}
+
+// Token of the tile's key k (−1 past the keys).
+__device__ __forceinline__ int32_t tile_key_token(const AttnArgs &a, int64_t base, int64_t jt, int64_t j1, int k) {
+  const int64_t j = jt + k;
+  if (base >= 0) return j < j1 ? (int32_t)(base + k) : -1;
+  return j < j1 ? (int32_t)key_token(a, j) : -1;
+}
+
+// Byte offset inside a buffer, or one past every buffer (the load returns 0)
+// for a key past the keys.
+__device__ __forceinline__ uint32_t key_offset(int32_t tok, uint32_t row_bytes, uint32_t col) {
+  return tok < 0 ? 0x80000000u : __umul24((uint32_t)tok, row_bytes) + col;
+}
+
+// Tokens are below 2^24 and every tensor below 2^31 bytes (checked on the
+// host), so offsets are 32-bit and the loads are buffer loads whose range
+// check turns the keys past the end into zeros.
 template <bool BF16>
-__device__ __forceinline__ void tile_fetch(TileIn<BF16> &f, const AttnArgs &a, int h, int64_t j0,
+__device__ __forceinline__ void tile_fetch(TileIn<BF16> &f, const AttnArgs &a, int h, int64_t jt,
                                            int64_t j1) {
   const int t = threadIdx.x;
   const int kk = t & 63, c = t >> 6, kp = t & 31, db = t >> 5;
-  const int64_t HD = a.heads * kAD;
-  {
-    const int64_t j = j0 + kk;
-    const int64_t tok = j < j1 ? key_token(a, j) : -1;
-    if constexpr (!BF16) {
-      f.kcode = u32x4{0u, 0u, 0u, 0u};
-      f.kscale = 0u;
-      if (tok >= 0) {
-        const int64_t e = tok * HD + (int64_t)h * kAD;             // element index of the row
-        f.kcode = *reinterpret_cast<const u32x4 *>(a.kc + e / 2 + 16 * c);
-        f.kscale = *reinterpret_cast<const uint16_t *>(a.ks + e / 16 + 2 * c);
-      }
-    } else {
+  const int64_t base = tile_run_token(a, jt, j1);
+  const int32_t tk = tile_key_token(a, base, jt, j1, kk);
+  const int32_t tv0 = tile_key_token(a, base, jt, j1, 2 * kp);
+  const int32_t tv1 = tile_key_token(a, base, jt, j1, 2 * kp + 1);
+  f.tok = tk;
+  if constexpr (!BF16) {
+    const uint32_t hd = (uint32_t)a.heads * kAD;                     // elements per token
+    const uint32_t cb = (uint32_t)a.kv_tokens * (hd / 2), sb = (uint32_t)a.kv_tokens * (hd / 16);
+    const __amdgpu_buffer_rsrc_t kc = buffer_rsrc(a.kc, cb), ks = buffer_rsrc(a.ks, sb);
+    const __amdgpu_buffer_rsrc_t vc = buffer_rsrc(a.vc, cb), vs = buffer_rsrc(a.vs, sb);
+    const uint32_t hc = (uint32_t)h * (kAD / 2), hs = (uint32_t)h * (kAD / 16);
+    f.kcode = __builtin_amdgcn_raw_buffer_load_b128(kc, (int)key_offset(tk, hd / 2, hc + 16 * c), 0, 0);
+    f.kscale = __builtin_amdgcn_raw_buffer_load_b16(ks, (int)key_offset(tk, hd / 16, hs + 2 * c), 0, 0);
+    f.vcode[0] = __builtin_amdgcn_raw_buffer_load_b64(vc, (int)key_offset(tv0, hd / 2, hc + 8 * db), 0, 0);
+    f.vcode[1] = __builtin_amdgcn_raw_buffer_load_b64(vc, (int)key_offset(tv1, hd / 2, hc + 8 * db), 0, 0);
+    f.vscale[0] = __builtin_amdgcn_raw_buffer_load_b8(vs, (int)key_offset(tv0, hd / 16, hs + db), 0, 0);
+    f.vscale[1] = __builtin_amdgcn_raw_buffer_load_b8(vs, (int)key_offset(tv1, hd / 16, hs + db), 0, 0);
+  } else {
+    const uint32_t rowb = (uint32_t)a.ldkv * 2, nb = (uint32_t)a.kv_tokens * rowb;
+    const __amdgpu_buffer_rsrc_t kb = buffer_rsrc(a.kb, nb), vb = buffer_rsrc(a.vb, nb);
+    const uint32_t hb = (uint32_t)h * (kAD * 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.kraw[i] = u32x4{0u, 0u, 0u, 0u};
-      if (tok >= 0) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.kb + tok * a.ldkv + (int64_t)h * kAD + 32 * c);
+    for (int i = 0; i < 4; ++i)
+      f.kraw[i] = __builtin_amdgcn_raw_buffer_load_b128(kb, (int)key_offset(tk, rowb, hb + 64 * c + 16 * i), 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) f.kraw[i] = p[i];
-      }
-    }
-    f.tok = tok;
-  }
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t j = j0 + 2 * kp + q;
-    const int64_t tok = j < j1 ? key_token(a, j) : -1;
-    if constexpr (!BF16) {
-      f.vcode[q] = u32x2{0u, 0u};
-      f.vscale[q] = 0u;
-      if (tok >= 0) {
-        const int64_t e = tok * HD + (int64_t)h * kAD;
-        f.vcode[q] = *reinterpret_cast<const u32x2 *>(a.vc + e / 2 + 8 * db);
-        f.vscale[q] = a.vs[e / 16 + db];
-      }
-    } else {
-      f.vraw[q][0] = f.vraw[q][1] = u32x4{0u, 0u, 0u, 0u};
-      if (tok >= 0) {
-        const u32x4 *p = reinterpret_cast<const u32x4 *>(a.vb + tok * a.ldkv + (int64_t)h * kAD + 16 * db);
-        f.vraw[q][0] = p[0];
-        f.vraw[q][1] = p[1];
-      }
+    for (int i = 0; i < 2; ++i) {
+      f.vraw[0][i] = __builtin_amdgcn_raw_buffer_load_b128(vb, (int)key_offset(tv0, rowb, hb + 32 * db + 16 * i), 0, 0);
+      f.vraw[1][i] = __builtin_amdgcn_raw_buffer_load_b128(vb, (int)key_offset(tv1, rowb, hb + 32 * db + 16 * i), 0, 0);
     }
   }
 }
@@ -239,10 +263,10 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, c
     if (f.tok >= 0) {
       if constexpr (!BF16) {
         if (f.tok < cc.lo || f.tok >= cc.hi) {
-          const int64_t ci = lds_starts != nullptr ? attn_chunk_of(lds_starts, a.n_chunks, f.tok)
-                                                   : attn_chunk_of(a.chunk_start, a.n_chunks, f.tok);
-          cc.lo = lds_starts != nullptr ? (int64_t)lds_starts[ci] : a.chunk_start[ci];
-          cc.hi = lds_starts != nullptr ? (int64_t)lds_starts[ci + 1] : a.chunk_start[ci + 1];
+          const int64_t ci = lds_starts != nullptr ? attn_chunk_of(lds_starts, a.n_chunks, (int64_t)f.tok)
+                                                   : attn_chunk_of(a.chunk_start, a.n_chunks, (int64_t)f.tok);
+          cc.lo = lds_starts != nullptr ? lds_starts[ci] : (int32_t)a.chunk_start[ci];
+          cc.hi = lds_starts != nullptr ? lds_starts[ci + 1] : (int32_t)a.chunk_start[ci + 1];
           cc.gk = a.gscale[2 * ci] * a.qk_scale;
           cc.gv = a.gscale[2 * ci + 1];
         }
@@ -325,7 +349,6 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
       if (jt + 2 * kAK < j1) tile_fetch<BF16>(fin, a, h, jt + 2 * kAK, j1);
     }
     const AttnTile &B = L.buf[cur];
-    const int kvalid = (j1 - jt) < kAK ? (int)(j1 - jt) : kAK;
 
     // Sᵀ = K·Qᵀ: lane (query r, hh) gets keys 32kb + 8(v/4) + 4hh + v%4
     f32x16 s[2];
@@ -343,47 +366,65 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
       }
       s[kb] = acc;
     }
-    // scale by each key's g_K · scale · log2(e); mask keys past the split
+    // Softmax in base 2 against a reference m that moves lazily: m (and with
+    // it O and l) moves only when some query of the wave sees a scaled score
+    // more than 2^kLazy above it, so p = 2^(s·g_K − m) stays below 2^kLazy.
+    // Any reference gives the same result: O and l carry the same factor, and
+    // the split merge uses m.  Keys past the split (only in its last tile)
+    // score −inf.
+    const int kvalid = (j1 - jt) < kAK ? (int)(j1 - jt) : kAK;
     float mt = -__builtin_huge_valf();
+    if (kvalid == kAK) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int key0 = 32 * kb + 8 * g4 + 4 * hh;
-        const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[key0]);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[32 * kb + 8 * g4 + 4 * hh]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float tv = s[kb][4 * g4 + e] * gk4[e];
-          if (kvalid < kAK && key0 + e >= kvalid) tv = -__builtin_huge_valf();
-          s[kb][4 * g4 + e] = tv;
-          mt = mt > tv ? mt : tv;
+          for (int e = 0; e < 4; ++e) {
+            const float tv = s[kb][4 * g4 + e] * gk4[e];
+            s[kb][4 * g4 + e] = tv;
+            mt = __builtin_fmaxf(mt, tv);
+          }
         }
-      }
-    {
-      const float other = __shfl_xor(mt, 32, 64);
-      mt = mt > other ? mt : other;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int key0 = 32 * kb + 8 * g4 + 4 * hh;
+          const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[key0]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float tv = key0 + e < kvalid ? s[kb][4 * g4 + e] * gk4[e] : -__builtin_huge_valf();
+            s[kb][4 * g4 + e] = tv;
+            mt = __builtin_fmaxf(mt, tv);
+          }
+        }
     }
-    const float m_new = m > mt ? m : mt;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    float psum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][v] - m_new);
-        s[kb][v] = p;
-        psum += p;
-      }
-    l = l * alpha + psum;
-    m = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32, 64));
+    if (__builtin_amdgcn_ballot_w64(mt > m + kLazy) != 0) {
+      const float m_new = __builtin_fmaxf(m, mt);
+      const float alpha = m == m_new ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+      m = m_new;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
     }
-    // Pᵀ fragments (times each key's g_V, rounded to bf16): slice sl holds
-    // keys 16sl + 8(i/4) + 4hh + i%4 for i = 0..7, registers 8(sl%2) + i of s[sl/2]
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float pv = __builtin_amdgcn_exp2f(s[kb][v] - m);
+        s[kb][v] = pv;
+        psum += pv;
+      }
+    l += psum;
+    // Pᵀ fragments (p·g_V rounded to bf16): slice sl holds keys
+    // 16sl + 8(i/4) + 4hh + i%4 for i = 0..7, registers 8(sl%2) + i of s[sl/2]
     bf16x8 pf[4];
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {

@@ -122,6 +122,8 @@ struct AttnArgs {
   int64_t n_chunks;
   const uint16_t *kb, *vb;              // bf16 twin: token t head h at kb + t·ldkv + 128·h
   int64_t ldkv;
+  int64_t kv_tokens;                    // tokens addressable in the K/V buffers (< 2^24,
+                                        // and each buffer below 2^31 bytes)
   int64_t range_lo[kAttnMaxRanges], range_len[kAttnMaxRanges];
   int n_ranges;
   int64_t Tk;

@@ -313,7 +313,9 @@ int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1,
  * Arithmetic: Q converted to fp16 (exact for |q| in [2^-14, 65504] or 0),
  * K·Q products exact and summed in fp32, times g_K·scale, base-2 online
  * softmax in fp32, P·g_V rounded to bf16, products with V (exact) summed in
- * fp32, one bf16 rounding of the output.  Requires |q| < 65504.
+ * fp32, one bf16 rounding of the output.  Requires |q| < 65504, and a cache
+ * of fewer than 2^24 filled tokens with at most 2^31 elements per tensor
+ * (NVFP4_EINVAL otherwise).
  */
 #define NVFP4_ATTN_MAX_RANGES 4
 int nvfp4_kv_attention_workspace(int64_t Tq, int64_t heads, int64_t Tk, size_t *bytes);
@@ -326,7 +328,8 @@ int nvfp4_kv_attention(const nvfp4_kv_cache *c, const uint16_t *Q, int64_t Tq, i
  * (token j, head h at K + j·ldkv + 128·h): the baseline against which the
  * fused dequantisation's cost is measured.  Q·K and P·V on the bf16 matrix
  * cores (P rounded to bf16), otherwise as nvfp4_kv_attention; the workspace
- * size is nvfp4_kv_attention_workspace(Tq, heads, Tk).
+ * size is nvfp4_kv_attention_workspace(Tq, heads, Tk).  Requires Tk < 2^24
+ * and Tk·ldkv <= 2^30 (K and V each below 2^31 bytes).
  */
 int nvfp4_attention_bf16(const uint16_t *Q, int64_t Tq, int64_t ldq, const uint16_t *K,
                          const uint16_t *V, int64_t Tk, int64_t ldkv, int64_t heads, float scale,

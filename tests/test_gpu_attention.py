@@ -6,8 +6,10 @@ Tolerance: the GPU path rounds two quantities to bf16, the probabilities
 times g_V before the P·V product and the output; everything else is exact
 (the dequantised K and V, Q in fp16, their products) or fp32.  Each bf16
 rounding is at most 2^-9 relative, so the output is checked against the
-oracle within ATTN_TOL = 2·2^-9 normwise, per head, and within the same bound
-against the oracle's own bf16 rounding.
+binary64 oracle within ATTN_TOL = 2·2^-9 normwise, per head.  The oracle's
+own bf16 rounding of that result is another 2^-9 away from it, so against the
+bf16-rounded oracle the bound is ATTN_TOL_BF16 = 3·2^-9 (a single key, where
+nothing averages out, reaches it).
 """
 
 import numpy as np
@@ -22,6 +24,7 @@ from gpu_helpers import announce, bf16_to_dev, to_bits
 pytestmark = pytest.mark.gpu
 
 ATTN_TOL = 2 * 2.0 ** -9
+ATTN_TOL_BF16 = 3 * 2.0 ** -9
 D = 128
 
 
@@ -60,7 +63,7 @@ def _check(o_bits, o64, o_ref_bits, label):
         e64 = np.linalg.norm(got[:, h] - o64[:, h]) / np.linalg.norm(o64[:, h])
         eref = np.linalg.norm(got[:, h] - ref[:, h]) / np.linalg.norm(ref[:, h])
         announce(f"  {label} head {h}: {e64:.3e} vs fp64, {eref:.3e} vs bf16 oracle")
-        assert e64 <= ATTN_TOL and eref <= ATTN_TOL, (label, h, e64, eref)
+        assert e64 <= ATTN_TOL and eref <= ATTN_TOL_BF16, (label, h, e64, eref)
 
 
 @pytest.mark.parametrize("sizes,Tq,ranges", [
