@@ -223,7 +223,9 @@ class KVCache:
 
     ``append(K, V)`` quantises a chunk of bf16 [T, heads, head_dim] keys and
     values into the cache (one pair of tensor scales per append);
-    ``dequant(t0, t1)`` returns bf16 K and V for tokens [t0, t1).
+    ``qkv_append(x, W…)`` runs the QKV projection and appends its K and V;
+    ``dequant(t0, t1)`` returns bf16 K and V for tokens [t0, t1);
+    ``attention(Q, ranges)`` attends over the cache in NVFP4.
     """
 
     def __init__(self, capacity: int, heads: int, head_dim: int, max_chunks: int, device="cuda"):
@@ -265,16 +267,16 @@ class KVCache:
         for t, name in ((K, "K"), (V, "V")):
             if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16:
                 raise TypeError(f"{name} must be a bf16 GPU tensor")
-        if K.is_contiguous() and V.is_contiguous():
+        if K.dim() == 3:
             _need(K, torch.bfloat16, "K", (T, self.desc.heads, self.desc.head_dim))
             _need(V, torch.bfloat16, "V", (T, self.desc.heads, self.desc.head_dim))
             ld = HD
         else:
             if K.dim() != 2 or tuple(K.shape) != (T, HD) or tuple(V.shape) != (T, HD):
-                raise ValueError(f"strided K/V must be 2-D [T, {HD}] row views")
+                raise ValueError(f"K/V must be [T, heads, head_dim] or 2-D [T, {HD}] row views")
             if K.stride(1) != 1 or V.stride(1) != 1 or K.stride(0) != V.stride(0):
-                raise ValueError("strided K/V need unit column stride and equal row strides")
-            ld = K.stride(0)
+                raise ValueError("K/V row views need unit column stride and equal row strides")
+            ld = K.stride(0) if T > 1 else max(K.stride(0), HD)
         if ws is None:
             if self._ws is None or self._ws.numel() < self.workspace_bytes(T):
                 self._ws = workspace(self.workspace_bytes(T), self.device)
@@ -282,6 +284,39 @@ class KVCache:
         qflags = NVFP4_Q_ADAPTIVE_4_6 if adaptive46 else 0
         check(lib().nvfp4_kv_append_ex(C.byref(self.desc), _ptr(K), _ptr(V), T, ld, qflags, _ptr(ws),
                                        ws.numel(), _stream(self.device)))
+
+    def qkv_workspace_bytes(self, T: int, D: int) -> int:
+        n = C.c_size_t()
+        check(lib().nvfp4_qkv_append_workspace(T, self.desc.heads, self.desc.head_dim, D, C.byref(n)))
+        return n.value
+
+    def qkv_append(self, x, Wq, Ws, Wg, bias=None, out=None, ws=None, adaptive46=False):
+        """nvfp4_qkv_append: the QKV projection of x (bf16 [T, D]) with NVFP4
+        weights [3·heads·head_dim, D] (Q, K, V rows stacked), its K and V
+        slices appended to the cache as one chunk.  Returns QKV bf16
+        [T, 3·heads·head_dim] (or writes ``out``)."""
+        _need(x, torch.bfloat16, "x")
+        if x.dim() != 2:
+            raise ValueError("x must be 2-D [T, D]")
+        T, D = x.shape
+        N = 3 * self.desc.heads * self.desc.head_dim
+        _need(Wq, torch.uint8, "Wq", (N, D // 2))
+        _need(Ws, torch.uint8, "Ws", (N, D // 16))
+        _need(Wg, torch.float32, "Wg", (1,))
+        if bias is not None:
+            _need(bias, torch.bfloat16, "bias", (N,))
+        if out is None:
+            out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+        _need(out, torch.bfloat16, "out", (T, N))
+        need = self.qkv_workspace_bytes(T, D)
+        if ws is None:
+            if getattr(self, "_qkv_ws", None) is None or self._qkv_ws.numel() < need:
+                self._qkv_ws = workspace(need, self.device)
+            ws = self._qkv_ws
+        qflags = NVFP4_Q_ADAPTIVE_4_6 if adaptive46 else 0
+        check(lib().nvfp4_qkv_append(C.byref(self.desc), _ptr(x), T, D, _ptr(Wq), _ptr(Ws), _ptr(Wg), _ptr(bias),
+                                     _ptr(out), qflags, _ptr(ws), ws.numel(), _stream(self.device)))
+        return out
 
     def attention(self, Q, ranges, scale=0.0, out=None, ws=None):
         """nvfp4_kv_attention: softmax(Q·Kᵀ·scale)·V over the cache tokens of

@@ -67,6 +67,9 @@ _SIGS = {
                             _p, _i64, _p, _sz, _p], C.c_int),
     "nvfp4_attention_bf16": ([_p, _i64, _i64, _p, _p, _i64, _i64, _i64, C.c_float, _p, _i64, _p, _sz, _p],
                              C.c_int),
+    "nvfp4_qkv_append_workspace": ([_i64, _i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
+    "nvfp4_qkv_append": ([C.POINTER(KVCacheDesc), _p, _i64, _i64, _p, _p, _p, _p, _p, C.c_uint32, _p, _sz, _p],
+                         C.c_int),
     "nvfp4_quantize_rht_workspace": ([_i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_quantize_rht": ([_p, _i64, _i64, _i64, C.c_uint32, _p, _p, _p, _p, _sz, _p], C.c_int),
     "nvfp4_testing_set_quantize_wait": ([C.c_uint64], C.c_uint64),

@@ -390,6 +390,89 @@ int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int
   return nvfp4_kv_append_ex(c, K, V, T, ld, 0u, ws, ws_bytes, stream);
 }
 
+// nvfp4_qkv_append workspace: [linear workspace | tile maxima | append scratch]
+// (the append scratch serves the unfused fallback)
+struct QkvWs {
+  LinearWs lin;
+  size_t slots, app, total;
+  int64_t max_tiles;
+};
+
+static QkvWs qkv_ws(int64_t T, int64_t N, int64_t D) {
+  QkvWs w;
+  w.lin = linear_ws(T, D);
+  w.max_tiles = ((T + 127) / 128) * ((N + 127) / 128);   // the finest tiling the GEMM uses
+  w.slots = w.lin.total;
+  w.app = round_up(w.slots + size_t(w.max_tiles) * sizeof(uint32_t), 256);
+  w.total = round_up(w.app + 2 * kQuantWs, 256);
+  return w;
+}
+
+int nvfp4_qkv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, int64_t D, size_t *bytes) {
+  if (bytes == nullptr) return fail(NVFP4_EINVAL, "bytes is NULL");
+  int s;
+  if ((s = check_mk(T, D, "qkv_append_workspace"))) return s;
+  if (heads < 1 || head_dim < 32 || head_dim % 32) return fail(NVFP4_EINVAL, "qkv_append_workspace: bad heads or head_dim");
+  const int64_t N = 3 * heads * head_dim;
+  if (N > kMaxElements / D || T > kMaxElements / N) return fail(NVFP4_EINVAL, "qkv_append_workspace: problem too large");
+  *bytes = qkv_ws(T, N, D).total;
+  return NVFP4_OK;
+}
+
+int nvfp4_qkv_append(nvfp4_kv_cache *c, const uint16_t *x, int64_t T, int64_t D, const uint8_t *Wq,
+                     const uint8_t *Ws, const float *Wg, const uint16_t *bias, uint16_t *QKV,
+                     uint32_t qflags, void *ws, size_t ws_bytes, void *stream) {
+  int s;
+  if ((s = check_cache(c, "qkv_append"))) return s;
+  if (qflags & ~NVFP4_Q_ADAPTIVE_4_6) return fail(NVFP4_EINVAL, "qkv_append: unknown flags");
+  size_t need = 0;
+  if ((s = nvfp4_qkv_append_workspace(T, c->heads, c->head_dim, D, &need))) return s;
+  const int64_t hd = c->heads * c->head_dim, N = 3 * hd;
+  if ((s = check_gemm_args(nullptr, nullptr, nullptr, Wq, Ws, Wg, bias, QKV, T, N, D, 0u, false))) return s;
+  if ((s = check_ptr(x, "x"))) return s;
+  if (T > c->capacity - c->n_tokens) return fail(NVFP4_ECAPACITY, "qkv_append: token capacity exceeded");
+  if (c->n_chunks >= c->max_chunks) return fail(NVFP4_ECAPACITY, "qkv_append: no chunk slot left");
+  if (ws == nullptr || ws_bytes < need) return fail(NVFP4_EWORKSPACE, "qkv_append: workspace too small");
+  if ((s = check_ptr(ws, "ws"))) return s;
+  const QkvWs w = qkv_ws(T, N, D);
+  uint8_t *base = static_cast<uint8_t *>(ws);
+  uint8_t *aq = base + w.lin.codes;
+  uint8_t *as = base + w.lin.scales;
+  float *ag = reinterpret_cast<float *>(base + w.lin.gscale);
+  uint32_t *slots = reinterpret_cast<uint32_t *>(base + w.slots);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  nvfp4::QuantJob jx{x, aq, as, ag, base + w.lin.partials, T, D, D};
+  if ((s = launched(nvfp4::launch_quantize(&jx, 1, st), st, "qkv_append/quantize"))) return s;
+  nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, QKV, T, N, D, 0u};
+  int bm = 0, bn = 0;
+  nvfp4::gemm_tile_of(a, &bm, &bn);
+  // fused when every tile's columns lie inside one of Q, K, V
+  const bool fused = hd % bn == 0;
+  if (fused) {
+    a.tile_amax = slots;
+    if (nvfp4::gemm_tile_count(a) > w.max_tiles) return fail(NVFP4_EHIP, "qkv_append: internal tile count exceeds the workspace");
+  }
+  if ((s = launched(nvfp4::launch_gemm(a, st), st, "qkv_append/gemm"))) return s;
+  const int64_t off = c->n_tokens * hd;
+  nvfp4::QuantJob jobs[2] = {
+      {QKV + hd, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, base + w.app, T, hd, N},
+      {QKV + 2 * hd, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
+       base + w.app + kQuantWs, T, hd, N}};
+  const nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
+  const bool adapt = (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0;
+  if (fused) {
+    const int64_t tiles_m = (T + bm - 1) / bm, per = (hd / bn) * tiles_m;
+    const uint32_t *const maxima[2] = {slots + per, slots + 2 * per};
+    s = launched(nvfp4::launch_encode2_from_partials(jobs, maxima, per, mark, adapt, st), st, "qkv_append/encode");
+  } else {
+    s = launched(nvfp4::launch_quantize(jobs, 2, st, &mark, adapt), st, "qkv_append/append");
+  }
+  if (s) return s;
+  c->n_tokens += T;
+  c->n_chunks += 1;
+  return NVFP4_OK;
+}
+
 int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1, uint16_t *K_out,
                      uint16_t *V_out, void *stream) {
   int s;

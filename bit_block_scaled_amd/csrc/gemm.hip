@@ -56,6 +56,12 @@ static TileChoice tile_of(const GemmArgs &a) {
   return tf ? by_flag[tf] : choose_tile(a.M, a.N);
 }
 
+void gemm_tile_of(const GemmArgs &a, int *bm, int *bn) {
+  const TileChoice c = tile_of(a);
+  *bm = 64 * c.wm;
+  *bn = 64 * c.wn;
+}
+
 int64_t gemm_tile_count(const GemmArgs &a) {
   const TileChoice c = tile_of(a);
   const int64_t bm = 64 * c.wm, bn = 64 * c.wn;

@@ -476,7 +476,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) k_gemm(GemmArgs a, int tiles_
       uint32_t mx = tred[0];
 #pragma unroll
       for (int w = 1; w < kGemmThreads / 64; ++w) mx = mx > tred[w] ? mx : tred[w];
-      a.tile_amax[t] = mx;
+      // column-major over tiles: the tiles of one column range are contiguous
+      a.tile_amax[(cn0 / BN) * tiles_m + cm0 / BM] = mx;
     }
   }
   if (t_next >= ntiles) break;

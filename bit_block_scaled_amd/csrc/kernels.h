@@ -50,6 +50,13 @@ struct ChunkMark {
 hipError_t launch_encode_from_partials(const QuantJob &job, const uint32_t *maxima, int64_t nparts,
                                        hipStream_t stream);
 
+// The same for two tensors in one launch (a KV append: K and V), each with its
+// own nparts maxima, with the KV-cache bookkeeping `mark` and optionally the
+// adaptive {4, 6} block scales.
+hipError_t launch_encode2_from_partials(const QuantJob (&jobs)[2], const uint32_t *const (&maxima)[2],
+                                        int64_t nparts, const ChunkMark &mark, bool adaptive46,
+                                        hipStream_t stream);
+
 // Bounded wait of the single-launch quantiser for the other workgroups'
 // maxima, in ticks of the 100 MHz real-time counter; returns the previous
 // value.  The results do not depend on it (a workgroup whose wait expires
@@ -77,12 +84,17 @@ struct GemmArgs {
   int64_t M, N, K;
   uint32_t flags;
   // optional: every workgroup tile writes the largest magnitude of its stored
-  // outputs (the 15-bit pattern of the bf16 result) to tile_amax[tile]; the
-  // array has gemm_tile_count(...) entries
+  // outputs (the 15-bit pattern of the bf16 result) to
+  // tile_amax[tn · tiles_m + tm] for the tile in tile row tm, tile column tn
+  // (column-major, so the tiles of a range of output columns are
+  // contiguous); the array has gemm_tile_count(...) entries
   uint32_t *tile_amax = nullptr;
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t stream);
+
+// Workgroup tile (bm x bn) launch_gemm uses for these arguments.
+void gemm_tile_of(const GemmArgs &a, int *bm, int *bn);
 
 // Number of workgroup tiles launch_gemm uses for these arguments.
 int64_t gemm_tile_count(const GemmArgs &a);

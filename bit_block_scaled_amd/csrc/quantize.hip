@@ -718,6 +718,32 @@ hipError_t launch_encode_from_partials(const QuantJob &job, const uint32_t *maxi
   return hipGetLastError();
 }
 
+hipError_t launch_encode2_from_partials(const QuantJob (&jobs)[2], const uint32_t *const (&maxima)[2],
+                                        int64_t nparts, const ChunkMark &mark, bool adaptive46,
+                                        hipStream_t stream) {
+  QuantArgs a{};
+  a.mark = mark;
+  int64_t max_units = 0;
+  for (int i = 0; i < 2; ++i) {
+    a.t[i].x = jobs[i].x;
+    a.t[i].codes = jobs[i].codes;
+    a.t[i].scales = reinterpret_cast<uint16_t *>(jobs[i].scales);
+    a.t[i].gscale = jobs[i].gscale;
+    a.t[i].partials = const_cast<uint32_t *>(maxima[i]);
+    a.t[i].units = jobs[i].rows * (jobs[i].cols / 32);
+    a.t[i].units_per_row = (uint32_t)(jobs[i].cols / 32);
+    a.t[i].ld = jobs[i].ld;
+    if (a.t[i].units > max_units) max_units = a.t[i].units;
+  }
+  if (nparts < 1 || nparts > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid(encode_blocks(max_units), 2);
+  if (adaptive46)
+    hipLaunchKernelGGL(k_encode<true>, grid, dim3(kThreads), 0, stream, a, (int)nparts);
+  else
+    hipLaunchKernelGGL(k_encode<false>, grid, dim3(kThreads), 0, stream, a, (int)nparts);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
                            const ChunkMark *mark, bool adaptive46, bool blocks2d) {
   QuantArgs a{};

@@ -279,6 +279,33 @@ int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int
 int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int64_t T,
                        int64_t ld, uint32_t qflags, void *ws, size_t ws_bytes, void *stream);
 
+/* Workspace bytes nvfp4_qkv_append needs (zero before its first use, as for
+ * nvfp4_linear; the library keeps it valid from one call to the next). */
+int nvfp4_qkv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, int64_t D, size_t *bytes);
+
+/*
+ * The QKV projection of T tokens with its K and V appended to the cache, in
+ * three launches: quantise x, the W4A4 GEMM, and one encode of the K and V
+ * column slices of its output into the cache.  Source: 二、方法 / 推理底座 (W4A4
+ * inference; the KV cache is quantised to NVFP4 per chunk as it is written).
+ * The result equals nvfp4_linear followed by nvfp4_kv_append_ex on the K and
+ * V slices of its output (ld = 3·heads·head_dim), byte for byte, but the
+ * append's tensor amax comes from the GEMM epilogue (the largest stored
+ * |output| of each workgroup tile), so no pass over K and V precedes the
+ * encode.  If the GEMM's tile width does not divide heads·head_dim, the
+ * append runs as nvfp4_kv_append_ex does (same bytes, one more pass).
+ *   x      bf16 [T, D] activations, 16-byte aligned, D % 32 == 0
+ *   Wq/Ws/Wg  NVFP4 weights [3·heads·head_dim, D]: the Q rows, then K, then V
+ *   bias   bf16 [3·heads·head_dim] or NULL
+ *   QKV    out: bf16 [T, 3·heads·head_dim] (Q for the attention, ldq = 3·heads·head_dim)
+ *   qflags 0 or NVFP4_Q_ADAPTIVE_4_6 for the appended K and V
+ *   ws     nvfp4_qkv_append_workspace(T, heads, head_dim, D) bytes
+ * Errors as nvfp4_linear and nvfp4_kv_append_ex (cache unchanged on error).
+ */
+int nvfp4_qkv_append(nvfp4_kv_cache *c, const uint16_t *x, int64_t T, int64_t D, const uint8_t *Wq,
+                     const uint8_t *Ws, const float *Wg, const uint16_t *bias, uint16_t *QKV,
+                     uint32_t qflags, void *ws, size_t ws_bytes, void *stream);
+
 /*
  * Dequantise tokens [t0, t1) of K and V to bf16 [t1-t0, heads, head_dim]:
  *   out = bf16( fl32( fl32(E2M1 · E4M3) · g_chunk ) )

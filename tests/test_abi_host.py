@@ -250,3 +250,29 @@ def test_quantize_rht_rejects(L):
     assert call(wsb=16) == EWS
     assert call(ws=None) == EWS
     assert b"quantize_rht" in L.nvfp4_last_error()
+
+
+def test_qkv_append_rejects(L):
+    d = _desc()
+    assert L.nvfp4_kv_init(C.byref(d)) == 0
+    n = C.c_size_t()
+    assert L.nvfp4_qkv_append_workspace(880, 24, 128, 3072, C.byref(n)) == 0
+    need = n.value
+    assert need >= 880 * 3072 // 2                          # holds the quantised activations
+    assert L.nvfp4_qkv_append_workspace(880, 24, 100, 3072, C.byref(n)) == EINVAL
+    assert L.nvfp4_qkv_append_workspace(880, 24, 128, 3000, C.byref(n)) == EINVAL
+    f = L.nvfp4_qkv_append
+    args = [C.byref(d), FAKE, 10, 3072, FAKE, FAKE, FAKE, None, FAKE, 0, FAKE, need, None]
+    def call(i, v):
+        a = list(args)
+        a[i] = v
+        return f(*a)
+    assert call(9, 0x80) == EINVAL                           # unknown flag
+    assert call(1, MIS) == EINVAL                            # x misaligned
+    assert call(8, None) == EINVAL                           # no output
+    assert call(3, 3000) == EINVAL                           # D % 32
+    assert call(11, 64) == EWS                               # workspace too small
+    assert call(2, 101) == ECAP                              # 101 tokens into a 100-token cache
+    d.n_chunks = 4
+    assert f(*args) == ECAP                                  # no chunk slot
+    assert d.n_tokens == 0 and d.n_chunks == 4               # unchanged on error
