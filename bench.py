@@ -20,8 +20,9 @@ device synchronisations.  The same step is also run eagerly K times with an
 event after every kernel (the library's launch-event testing hook), which
 gives the per-kernel breakdown and the dominant kernel's roofline (the up
 GEMM).  Further entries in `kernels` time the other configurations' kernels
-(QKV and long-context GEMMs and quantisers, the 65536-token KV append
-sequence and its read-back, attention of an 880-token query chunk over that
+(QKV and long-context GEMMs and quantisers, an 880-token frame step of QKV
+projection + KV append with the append fused into the projection or not, the
+65536-token KV append sequence and its read-back, attention of an 880-token query chunk over that
 cache read in NVFP4 against the same kernel on bf16 K/V, the FFN up
 projection's weight gradient with Hadamard-transformed operands, a 1 GiB
 device copy) with p10/p50/p90 over repetitions; the HBM-bound ones after a
@@ -453,6 +454,44 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
             del kv, ko, vo
         del xd, wq, aq, asc, Cm, qws, wl
         torch.cuda.empty_cache()
+
+    # one frame step of the DiT at 880 tokens, 75 frames back to back: the QKV
+    # projection alone, then with its K/V appended to the NVFP4 cache by a
+    # separate append, then by nvfp4_qkv_append (the append encoded from the
+    # GEMM's tile maxima)
+    log("extras: 880-token frame step (QKV projection + KV append)")
+    qf = workloads.qkv(M=880)
+    xf, wqf, bf = up(qf.x), nv.quantize(up(qf.w)), up(qf.bias)
+    frames = 75
+    cf = nv.KVCache(880 * frames, 24, 128, max_chunks=frames, device=dev)
+    cp = nv.KVCache(880 * frames, 24, 128, max_chunks=frames, device=dev)
+    of = torch.empty((880, 9216), dtype=torch.bfloat16, device=dev)
+    lwsf = nv.workspace(nv.linear_workspace_bytes(880, 3072), dev)
+
+    def seq_linear():
+        for _ in range(frames):
+            nv.linear(xf, *wqf, bias=bf, out=of, ws=lwsf)
+
+    def seq_unfused():
+        cp.reset()
+        for _ in range(frames):
+            nv.linear(xf, *wqf, bias=bf, out=of, ws=lwsf)
+            cp.append(of[:, 3072:6144], of[:, 6144:])
+
+    def seq_fused():
+        cf.reset()
+        for _ in range(frames):
+            cf.qkv_append(xf, *wqf, bias=bf, out=of)
+    per = {}
+    for name, fn in (("linear_only", seq_linear), ("linear_then_append", seq_unfused), ("qkv_append", seq_fused)):
+        t = [v / frames for v in time_us(torch, fn, 5, 1)]
+        per[name] = float(np.median(t))
+        kernels[f"qkv880_frame_{name}"] = {"frames": frames, "us_per_frame": pct(t)}
+    kernels["qkv880_frame_append_cost"] = {
+        "unfused_us": round(per["linear_then_append"] - per["linear_only"], 2),
+        "fused_us": round(per["qkv_append"] - per["linear_only"], 2)}
+    del qf, xf, wqf, bf, cf, cp, of, lwsf
+    torch.cuda.empty_cache()
 
     # the 65536-token KV cache: 74 appends of 880 tokens + one of 416, then a
     # read-back of the whole cache
