@@ -339,6 +339,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t *red) {
 
 constexpr int kResThreads = 1024;            // one workgroup per CU
 constexpr int kStreamU = 2;                   // streamed blocks per thread per round
+constexpr int kLdsBlocks = 4;                 // STREAM: resident blocks per thread held in LDS (128 KB)
 
 // This thread's part of the |x| maximum of workgroup p's share of a tensor
 // (the blocks that workgroup p loads, including its streamed chunks): read by
@@ -386,12 +387,15 @@ __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
 // slot is never tagged with an epoch later than the word: a slot left by an
 // earlier call is never taken for a current one.  Because the word lives in
 // device memory, each replay of a captured graph gets a new epoch.
-// STREAM (one tensor, UMAX = 8): the tensor is larger than the registers of
-// the grid hold.  Its first nwg·1024·u blocks stay resident as above; the rest
-// is dealt to the workgroups in chunks of 1024 consecutive blocks, read once
-// for the maximum and once more to encode (from the MALL when it fits there).
-// Only that remainder is read twice, where the two-pass kernels read the whole
-// tensor twice.
+// STREAM (one tensor, UMAX = 8, u = 8 + kLdsBlocks): the tensor is larger
+// than the registers of the grid hold.  Its first nwg·1024·u blocks stay
+// resident, blocks 0..7 of a thread in registers as above and blocks
+// 8..8+kLdsBlocks−1 in LDS (loaded first, while the registers are free, each
+// thread reading back only what it stored); the rest is dealt to the
+// workgroups in chunks of 1024 consecutive blocks, read once for the maximum
+// and once more to encode (from the MALL when it fits there).  Only that
+// remainder is read twice, where the two-pass kernels read the whole tensor
+// twice.
 template <int NJ, int UMAX, bool ADAPT, bool STREAM = false>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
                                                                 int u, uint64_t wait_ticks) {
@@ -400,11 +404,36 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
   uint64_t epoch = (load_slot(ctrl) + 1) & kEpochMask;
   if (epoch == 0) epoch = 1;
   constexpr int NW = kResThreads / 64;
+  constexpr int ULDS = STREAM ? kLdsBlocks : 0;
   __shared__ uint32_t red[NJ][NW], red2[NJ][NW];
   __shared__ uint64_t miss[NJ][NW];
+  // LDS-resident blocks, [block][half][thread]: each wave's 16-byte stores and
+  // loads cover consecutive addresses
+  __shared__ u32x4 lds_blk[STREAM ? 2 * kLdsBlocks * kResThreads : 1];
   const int k = blockIdx.x, nwg = gridDim.x;
 
-  uint32_t w[NJ][UMAX][8], bm[NJ][UMAX];
+  // LDS-resident blocks: loaded straight into LDS (no registers held), lane
+  // l of a wave into slot l of the wave's 64-slot run; lanes past the tensor
+  // load nothing, and their slots are never read
+  if constexpr (STREAM) {
+    const QuantTensor &T = args.t[0];
+    const int wave_base = threadIdx.x & ~63;
+#pragma unroll
+    for (int i = 0; i < ULDS; ++i) {
+      const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + threadIdx.x;
+      if (UMAX + i < u && b < 2 * T.units) {
+        const u32x4 *p = block_src(T, b);
+#if defined(__HIP_DEVICE_COMPILE__)      // device-only builtin; the host pass only parses the kernel
+        __builtin_amdgcn_global_load_lds(p, &lds_blk[(2 * i) * kResThreads + wave_base], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(p + 1, &lds_blk[(2 * i + 1) * kResThreads + wave_base], 16, 0, 0);
+#endif
+      }
+    }
+  }
+
+  // (block maxima are recomputed at encode time rather than kept: eight
+  // registers fewer through the poll)
+  uint32_t w[NJ][UMAX][8];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const QuantTensor &T = args.t[j];
@@ -422,7 +451,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
     }
   }
   // streamed blocks (STREAM): b = nwg·u·1024 + (s·nwg + k)·1024 + thread
-  uint32_t ms = 0;
+  uint32_t ms = 0, ml = 0;
   if constexpr (STREAM) {
     const QuantTensor &T = args.t[0];
     const int64_t nb = 2 * T.units, cstride = (int64_t)nwg * kResThreads;
@@ -445,14 +474,29 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
         ms = ms > am ? ms : am;
       }
     }
+    // every load of this wave has landed (the direct-to-LDS ones included)
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_s_waitcnt(0);
+#endif
+#pragma unroll
+    for (int i = 0; i < ULDS; ++i) {
+      const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + threadIdx.x;
+      if (UMAX + i < u && b < nb) {
+        const u32x4 lo4 = lds_blk[(2 * i) * kResThreads + threadIdx.x];
+        const u32x4 hi4 = lds_blk[(2 * i + 1) * kResThreads + threadIdx.x];
+        const uint32_t wv[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+        const uint32_t am = absmax16(wv);
+        ml = ml > am ? ml : am;
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    uint32_t m = STREAM ? ms : 0u;
+    uint32_t m = STREAM ? (ms > ml ? ms : ml) : 0u;
 #pragma unroll
     for (int i = 0; i < UMAX; ++i) {
-      bm[j][i] = absmax16(w[j][i]);
-      m = m > bm[j][i] ? m : bm[j][i];
+      const uint32_t am = absmax16(w[j][i]);
+      m = m > am ? m : am;
     }
     const uint32_t bmax = block_max_u32<kResThreads>(m, red[j]);
     if (threadIdx.x == 0)
@@ -550,7 +594,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
     for (int i = 0; i < UMAX; ++i) {
       const int64_t b = ((int64_t)k * u + i) * kResThreads + threadIdx.x;
       uint32_t lo, hi;
-      const uint32_t S = encode_any<ADAPT>(w[j][i], bm[j][i], b6, b4, lo, hi);
+      const uint32_t S = encode_any<ADAPT>(w[j][i], absmax16(w[j][i]), b6, b4, lo, hi);
       if (i < u && b < 2 * T.units) {
         codes[b] = u32x2{lo, hi};
         scales[b] = (uint8_t)S;
@@ -558,6 +602,23 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
     }
     if constexpr (STREAM) {
       const int64_t nb = 2 * T.units, cstride = (int64_t)nwg * kResThreads;
+      // the thread index made opaque, so these indices are recomputed here
+      // instead of being kept in registers (spilled) since the prologue
+      uint32_t tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+#pragma unroll
+      for (int i = 0; i < ULDS; ++i) {
+        const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + tid;
+        const u32x4 lo4 = lds_blk[(2 * i) * kResThreads + tid];
+        const u32x4 hi4 = lds_blk[(2 * i + 1) * kResThreads + tid];
+        const uint32_t wv[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+        uint32_t lo, hi;
+        const uint32_t S = encode_any<ADAPT>(wv, absmax16(wv), b6, b4, lo, hi);
+        if (UMAX + i < u && b < nb) {
+          codes[b] = u32x2{lo, hi};
+          scales[b] = (uint8_t)S;
+        }
+      }
       const int64_t chunk0 = cstride * u + (int64_t)k * kResThreads + threadIdx.x;
       for (int64_t b0 = chunk0; b0 < nb; b0 += kStreamU * cstride) {
         uint32_t v[kStreamU][8];
@@ -653,10 +714,14 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
   const uint64_t wt = g_wait_ticks.load();
   if (li == 4) {
     // more than the grid's registers hold: keep 8 blocks per thread resident
-    // and stream the rest (one tensor only; else the two-pass kernels)
+    // in registers and kLdsBlocks in LDS, and stream the rest (one tensor
+    // only; else the two-pass kernels)
     if (njobs != 1 || !lim.fits_stream[ADAPT]) return false;
+    // the fewest blocks per thread that cover the tensor (every workgroup
+    // busy), at most what registers and LDS hold
+    const int us = (int)(u < 8 + kLdsBlocks ? u : 8 + kLdsBlocks);
     hipLaunchKernelGGL((k_quant_resident<1, 8, ADAPT, true>), dim3((unsigned)nwg), dim3(kResThreads), 0,
-                       stream, a, 8, wt);
+                       stream, a, us, wt);
     *err = hipGetLastError();
     return true;
   }

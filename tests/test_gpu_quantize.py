@@ -121,11 +121,12 @@ def test_ffn_hidden_shape_sampled_rows():
     _check(hb, "H-shaped [8192,14336] sampled rows", rows=rows, amax=A)
 
 
-@pytest.mark.parametrize("M,K,seed", [(11000, 3072, 51), (81000, 416, 52)])
+@pytest.mark.parametrize("M,K,seed", [(11000, 3072, 51), (81000, 416, 52), (17000, 3072, 53)])
 def test_streamed_beyond_register_capacity(M, K, seed):
-    # just past what 256 workgroups x 1024 threads x 8 blocks hold: the first
-    # blocks stay in registers, the rest is streamed (read twice); whole-tensor
-    # bit-exactness, standard and adaptive, and with the wait forced to expire
+    # past what 256 workgroups x 1024 threads x 8 blocks hold in registers: the
+    # first two fit with 4 more blocks per thread in LDS, the third goes past
+    # those 12 and streams the rest (read twice); whole-tensor bit-exactness,
+    # standard and adaptive, and with the wait forced to expire
     x = workloads.random_matrix(seed, M, K, 1.0, outliers=True)
     _check(x, f"streamed {M}x{K}")
     codes, scales, g = nv.quantize(bf16_to_dev(x), adaptive46=True)
