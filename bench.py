@@ -511,6 +511,21 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
     kvb = 2 * T * 3072 * Q_BYTES_PER_ELEM + 8 * len(sizes)
     kernels["kv65536_append_sequence_cold"] = {"appends": len(sizes), "tokens": T, "us": pct(t),
                                                "roofline": roof_hbm(kvb, float(np.median(t)))}
+    # the same cache filled in the pages' KV chunks of 8 frames (9 appends of
+    # 7040 tokens and one of 2176)
+    sizes8 = workloads.kv_chunk_sizes(T, 8 * workloads.KV_CHUNK)
+    starts8 = np.r_[0, np.cumsum(sizes8)]
+    cache8 = nv.KVCache(T, 24, 128, max_chunks=len(sizes8), device=dev)
+
+    def seq8():
+        cache8.reset()
+        for i in range(len(sizes8)):
+            cache8.append(kd[starts8[i]:starts8[i + 1]], vd[starts8[i]:starts8[i + 1]])
+    t = time_us(torch, seq8, 10, 2, flush)
+    kernels["kv65536_append_8frame_chunks_cold"] = {"appends": len(sizes8), "tokens": T, "us": pct(t),
+                                                    "roofline": roof_hbm(2 * T * 3072 * Q_BYTES_PER_ELEM + 8 * len(sizes8),
+                                                                         float(np.median(t)))}
+    del cache8
     # each 880-token append inside the back-to-back sequence: an event after
     # every append, per-append time = the gap between consecutive events
     per = []

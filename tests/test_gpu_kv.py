@@ -99,6 +99,33 @@ def test_full_workload_every_chunk():
     assert nbytes * 8 == 9 * T * H * D
 
 
+@pytest.mark.parametrize("adaptive", [False, True])
+def test_eight_frame_chunks(adaptive):
+    # the pages' KV chunk of 8 frames (8 x 880 = 7040 tokens) as the append
+    # granularity: the 65536-token workload in 9 chunks of 7040 and one of
+    # 2176, every byte and the read-back bit-exact, with the adaptive {4, 6}
+    # scale selection the pages pair with it
+    K, V, _ = workloads.kv()
+    H, D = workloads.HEADS, workloads.HEAD_DIM
+    T = K.shape[0]
+    sizes = workloads.kv_chunk_sizes(T, 8 * workloads.KV_CHUNK)
+    announce(f"kv 8-frame chunks: {sizes[:2]}.. ({len(sizes)} appends), adaptive={adaptive}")
+    gpu = nv.KVCache(T, H, D, max_chunks=len(sizes))
+    kd, vd = bf16_to_dev(K), bf16_to_dev(V)
+    starts = np.r_[0, np.cumsum(sizes)]
+    for i in range(len(sizes)):
+        gpu.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]], adaptive46=adaptive)
+    ko, vo = gpu.dequant(0, T)
+    torch.cuda.synchronize()
+    del kd, vd
+    ref = oracle.KVCacheRef(T, H, D)
+    for i in range(len(sizes)):
+        ref.append(K[starts[i]:starts[i + 1]], V[starts[i]:starts[i + 1]], adaptive46=adaptive)
+    _compare_cache(gpu, ref, T)
+    rk, rv = ref.dequant(0, T)
+    assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
+
+
 def test_strided_append_from_fused_rows():
     # K and V read in place as column slices of a [T, 3·H·D] row-major matrix
     # (the layout of a fused QKV projection output), token stride 3·H·D
