@@ -17,25 +17,27 @@
 // is exact unless the group spans 2^41 or more in magnitude; each output is
 // rounded once to binary32 (an exact zero as +0: a sign-flipped zero input
 // would otherwise leave −0 in the sums).  The factor 1/4 is a power of two,
-// so the kernel keeps u = fl32(4y) and applies 1/4 exactly where y enters: the block amax
-// (a = max|u| / 4) and the reciprocal (u·(r/4) rounds like y·r).  The tensor
-// amax, the E4M3 block scales and the E2M1 codes then follow the binary32
-// steps of the NVFP4 quantiser.
+// so the kernel keeps u = fl32(4y) and applies 1/4 exactly where y enters:
+// the block amax (a = max|u| / 4) and the reciprocal (u·(r/4) rounds like
+// y·r).  The tensor amax, the E4M3 block scales and the E2M1 codes then follow
+// the binary32 steps of the NVFP4 quantiser.
 //
-// Layout of the work.  A workgroup pass covers 256 tokens × 16·kFeat features
-// with 256 threads; thread (group = tid/16, c = tid%16) holds the 16 tokens of
-// one group for kFeat consecutive features (16 loads of 2·kFeat bytes: one
-// wave reads four row segments of 32·kFeat bytes per load).  kFeat = 4 keeps
-// the encode kernel at three waves per SIMD (8 features need two, and lose
-// 7 % on the 8192 × 14336 operand; prefetching the next tile into registers
-// costs more occupancy than it hides).  Each of its
-// columns is exactly one NVFP4 block of the transpose, so block maxima need no
-// exchange between threads.  The code bytes (128 per feature) and scale bytes
-// (16 per feature) of the transpose are
-// staged in LDS and written as whole row segments.  Two launches: the first
-// writes one partial amax per workgroup; the second folds them into g, then
-// transforms again and encodes, visiting the tiles in reverse order so that
-// its first tiles are the ones the first launch read last (still in cache).
+// Layout of the work.  A workgroup pass covers 256 tokens × 16·kFeat
+// features with 256 threads; thread (group = tid/16, c = tid%16) holds the 16
+// tokens of one group for kFeat consecutive features (16 loads of 2·kFeat
+// bytes: one wave reads four row segments of 32·kFeat bytes per load).  Each
+// of its columns is exactly one NVFP4 block of the transpose, so block maxima
+// need no exchange between threads.  kFeat = 4 keeps the encode kernel at
+// three waves per SIMD (8 features need two and were 7 % slower on an
+// 8192 × 14336 operand; prefetching the next tile into registers cost more
+// occupancy than it hid).  The code bytes (128 per feature) and scale bytes
+// (16 per feature) of the transpose are staged in LDS and written as whole
+// row segments.
+//
+// Two launches, because the tensor amax of the transformed values precedes
+// every block scale: the first writes one partial amax per workgroup; the
+// second folds them into g, then transforms again and encodes, visiting the
+// tiles in reverse order (the first launch's last tiles first).
 #include "device_common.h"
 #include "kernels.h"
 
