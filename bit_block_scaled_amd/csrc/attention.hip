@@ -19,14 +19,17 @@
 // Scores are computed transposed, Sᵀ = K·Qᵀ (v_mfma_f32_32x32x16_f16, Q
 // converted from bf16 to fp16 once), so a lane holds 32 of one query's 64
 // scores and the other 32 sit in the lane 32 apart: the row maximum is an
-// in-lane reduction plus one exchange.  Online softmax in base 2 (exp2), P
-// times g_V rounded to bf16 (bf16 keeps the exponent range of small
-// probabilities), then Oᵀ += Vᵀ·Pᵀ (v_mfma_f32_32x32x16_bf16): the
+// in-lane reduction plus one exchange.  Online softmax in base 2 (exp2)
+// against a reference that moves only when a score would exceed it by more
+// than 2^kLazy (so the O rescale is rare), P times g_V rounded to bf16 (bf16
+// keeps the exponent range of small probabilities), then Oᵀ += Vᵀ·Pᵀ
+// (v_mfma_f32_32x32x16_bf16): the
 // accumulator registers of Sᵀ are already laid out as the B operand of that
 // product for the key order k = 16s + 8(i/4) + 4h + i%4, which the Vᵀ
 // fragment reads follow.  The tile after the current one is fetched from
-// global memory into registers while the current one is computed; the
-// decoded tiles alternate between two LDS buffers, one barrier per tile.
+// global memory into registers (32-bit offsets, buffer loads that return 0
+// past the keys) while the current one is computed; the decoded tiles
+// alternate between two LDS buffers, one barrier per tile.
 // With more than one split, each split writes its unnormalised O with its
 // running maximum and sum, and k_attn_combine merges them.
 //
