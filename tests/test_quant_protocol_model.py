@@ -11,7 +11,7 @@ This module simulates that exchange step by step: every workgroup is a
 generator that yields after each access to the shared workspace, and a
 scheduler decides which workgroup moves next, including workgroups that only
 start after others have finished (a grid that is not resident all at once).
-Two variants are modelled:
+Three variants are modelled:
 
   "advance_by_wg0"   the earlier kernel: workgroup 0 advances the control word
                      as soon as its own poll ends, whether it saw every slot or
@@ -23,6 +23,10 @@ Two variants are modelled:
                      no workgroup of a call can read an advanced word.  An
                      expired workgroup reads directly only the shares of the
                      workgroups whose slots it has not seen.
+
+  "arrive_before_read"  an arrival at the start, before the read of the
+                     control word, and the advance after the poll (a negative
+                     control).
 
 The tests show that the first variant takes a stale maximum from the previous
 call under a reachable schedule, and that the second gives every workgroup the
@@ -58,6 +62,12 @@ def wg_program(variant, k, shares, ws, wait_polls, out):
     The workgroup's result (its tensor maximum A) is stored in out[k].
     """
     nwg = len(shares)
+    last = False
+    if variant == "arrive_before_read":            # the order the current kernel avoids
+        old = ws.arrive
+        ws.arrive = old + 1
+        last = old == nwg - 1
+        yield
     epoch = (ws.eword + 1) & MASK48 or 1           # read the control word
     yield
     ws.slot[k] = (epoch, shares[k])                # publish this share's maximum
@@ -81,6 +91,13 @@ def wg_program(variant, k, shares, ws, wait_polls, out):
             ws.eword = epoch
             yield
         out[k] = max(seen.values()) if len(seen) == nwg else max(shares)
+    elif variant == "arrive_before_read":
+        if last:                                   # advance once the poll has ended
+            ws.arrive = 0
+            ws.eword = epoch
+            yield
+        direct = [shares[p] for p in range(nwg) if p not in seen]
+        out[k] = max(list(seen.values()) + direct)
     elif variant == "last_arrival":
         old = ws.arrive                            # one atomic add
         ws.arrive = old + 1
@@ -204,6 +221,24 @@ def test_random_schedules_find_the_earlier_race():
             shares = [rng.randint(0, 0x7F7F) for _ in range(nwg)]
             waits = [rng.choice([0, 1, 2, 5, LONG]) for _ in range(nwg)]
             got = run_call("advance_by_wg0", shares, ws, random_schedule(rng, nwg), waits)
+            failures += got != [max(shares)] * nwg
+    assert failures > 0
+
+
+def test_random_schedules_find_an_arrival_before_the_read():
+    # arriving before reading the control word lets the last arriver advance
+    # it while a late workgroup of the same call has still to read it; that
+    # workgroup then tags its slot with the next call's epoch.  The search
+    # reaches that failure, so the read-then-arrive order is what it checks.
+    rng = random.Random(321)
+    failures = 0
+    for trial in range(400):
+        ws = Workspace()
+        for call in range(6):
+            nwg = rng.randint(1, 6)
+            shares = [rng.randint(0, 0x7F7F) for _ in range(nwg)]
+            waits = [rng.choice([0, 1, 2, 5, LONG]) for _ in range(nwg)]
+            got = run_call("arrive_before_read", shares, ws, random_schedule(rng, nwg), waits)
             failures += got != [max(shares)] * nwg
     assert failures > 0
 
