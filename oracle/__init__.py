@@ -1,5 +1,6 @@
-"""CPU oracle for the NVFP4 W4A4 linear layer, the NVFP4 KV cache, attention
-over that cache and the Hadamard-transformed weight-gradient operands.
+"""CPU oracle for the NVFP4 W4A4 linear layer, the NVFP4 KV cache (with
+optional K-smoothing), attention over that cache and the Hadamard-transformed
+weight-gradient operands.
 
 TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously correct
 definition that the HIP path is checked against.  Only the test suite, the
@@ -45,6 +46,10 @@ Parity status per function:
   rht.*                  pinned (scipy's Hadamard matrix, exact rational brute force,
                          inverse, contraction invariance, hand-worked example; see
                          that module)
+  smooth.*, KVCacheRef(smooth_k=True)
+                         pinned (exact rational brute force of the centre, hand-worked
+                         tie, constant-channel and shift closed forms, permutation
+                         invariance, lossless round trip; see that module)
   The choices of global-scale formula, scale rounding mode, reciprocal-multiply
   order, nibble order, per-append KV scale and the binary32 error order of the
   adaptive selection are fixed by definition only
@@ -76,6 +81,7 @@ from .nvfp4 import (
 )
 from .attention import attention_ref, kv_attention_ref, range_tokens
 from .rht import hadamard, rht, rht_f64, quantize_rht
+from .smooth import k_center, smooth_keys
 
 __all__ = [
     "E2M1_VALUES",
@@ -104,4 +110,6 @@ __all__ = [
     "rht",
     "rht_f64",
     "quantize_rht",
+    "k_center",
+    "smooth_keys",
 ]

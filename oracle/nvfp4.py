@@ -60,6 +60,7 @@ from .formats import (
     pack_nibbles,
     unpack_nibbles,
 )
+from .smooth import k_center, smooth_keys
 
 BLOCK = 16                      # elements per E4M3 block scale
 E2M1_MAX = 6.0                  # largest E2M1 magnitude
@@ -269,10 +270,13 @@ class KVCacheRef:
 
     An append of T tokens quantises K and V, each viewed as [T·H, D], with
     :func:`quantize` (blocks of 16 along head_dim) and writes them at the
-    current token offset.
+    current token offset.  With ``smooth_k`` every append first takes the
+    centre of each key channel over its tokens and quantises the smoothed
+    keys instead (R33, R34, oracle/smooth.py); the centres are kept per
+    append in ``k_center`` ([H, D] bf16 bits each) and added back on read.
     """
 
-    def __init__(self, capacity: int, heads: int, head_dim: int):
+    def __init__(self, capacity: int, heads: int, head_dim: int, smooth_k: bool = False):
         if head_dim % 32:
             raise ValueError("head_dim must be a multiple of 32")
         self.cap, self.H, self.D = capacity, heads, head_dim
@@ -283,6 +287,8 @@ class KVCacheRef:
         self.gscale = []          # list of (g_K, g_V) float32
         self.chunk_start = [0]
         self.n_tokens = 0
+        self.smooth_k = bool(smooth_k)
+        self.k_center = []        # per append: [H, D] bf16 bits (smooth_k only)
 
     def append(self, k_bits: np.ndarray, v_bits: np.ndarray, adaptive46=False):
         T = k_bits.shape[0]
@@ -291,6 +297,10 @@ class KVCacheRef:
         if self.n_tokens + T > self.cap:
             raise ValueError("capacity exceeded")
         n = self.n_tokens
+        if self.smooth_k:
+            mu = k_center(k_bits)
+            self.k_center.append(mu)
+            k_bits = smooth_keys(k_bits, mu)
         kc, ks, kg = quantize(k_bits.reshape(T * self.H, self.D), adaptive46=adaptive46)
         vc, vs, vg = quantize(v_bits.reshape(T * self.H, self.D), adaptive46=adaptive46)
         self.k_codes[n:n + T] = kc.reshape(T, self.H, -1)
@@ -308,7 +318,9 @@ class KVCacheRef:
         """bf16 bits of K and V over tokens [t0, t1): [t1-t0, H, D] each.
 
         Each element is bf16(fl32(fl32(E2M1 · S) · g)): the first product is
-        exact in binary32, then one binary32 and one bf16 rounding.
+        exact in binary32, then one binary32 and one bf16 rounding.  Keys of
+        a smoothed cache get their append's centre added in binary32 before
+        the bf16 rounding (R35).
         """
         if not (0 <= t0 <= t1 <= self.n_tokens):
             raise ValueError("range outside the filled cache")
@@ -323,6 +335,10 @@ class KVCacheRef:
             es = (e * s).astype(np.float32)                       # exact
             g = np.array([self.gscale[ci][which] for ci in chunk], dtype=np.float32)
             v = (es * g[:, None, None]).astype(np.float32)        # fl32(·g)
+            if which == 0 and self.smooth_k:
+                mu = bf16_bits_to_f32(np.stack([self.k_center[ci] for ci in chunk])
+                                      if len(chunk) else np.zeros((0, self.H, self.D), np.uint16))
+                v = (v + mu).astype(np.float32)                   # fl32(· + μ)
             out.append(bf16_rne_from_f64(v.astype(np.float64)))
         return out[0], out[1]
 
@@ -332,7 +348,8 @@ class KVCacheRef:
     def values(self, tokens) -> tuple:
         """Exact dequantised K and V (binary64) of the given token indices:
         [len(tokens), H, D] each, E2M1 · S · g with the g of each token's
-        append (the dequant equation without any rounding)."""
+        append (the dequant equation without any rounding), plus the
+        append's centre for the keys of a smoothed cache (R36)."""
         tokens = np.asarray(tokens, dtype=np.int64)
         if tokens.size and (tokens.min() < 0 or tokens.max() >= self.n_tokens):
             raise ValueError("token outside the filled cache")
@@ -345,5 +362,8 @@ class KVCacheRef:
             e = np.where((c & 8) != 0, -mag, mag)
             s = np.repeat(e4m3_decode(scales[tokens]).astype(np.float64), BLOCK, axis=2)
             g = np.array([self.gscale[ci][which] for ci in chunk], dtype=np.float64)
-            out.append(e * s * g[:, None, None])
+            val = e * s * g[:, None, None]
+            if which == 0 and self.smooth_k and len(chunk):
+                val = val + bf16_bits_to_f32(np.stack([self.k_center[ci] for ci in chunk])).astype(np.float64)
+            out.append(val)
         return out[0], out[1]
