@@ -226,10 +226,16 @@ class KVCache:
     ``qkv_append(x, W…)`` runs the QKV projection and appends its K and V;
     ``dequant(t0, t1)`` returns bf16 K and V for tokens [t0, t1);
     ``attention(Q, ranges)`` attends over the cache in NVFP4.
+    With ``smooth_k`` every append centres each key channel first (the
+    centres are kept in ``k_center``, [max_chunks, heads, head_dim] bf16).
     """
 
-    def __init__(self, capacity: int, heads: int, head_dim: int, max_chunks: int, device="cuda"):
+    def __init__(self, capacity: int, heads: int, head_dim: int, max_chunks: int, device="cuda",
+                 smooth_k: bool = False):
         dev = torch.device(device)
+        self.smooth_k = bool(smooth_k)
+        self.k_center = (torch.zeros((max_chunks, heads, head_dim), dtype=torch.bfloat16, device=dev)
+                         if self.smooth_k else None)
         self.k_codes = torch.zeros((capacity, heads, head_dim // 2), dtype=torch.uint8, device=dev)
         self.v_codes = torch.zeros_like(self.k_codes)
         self.k_scales = torch.zeros((capacity, heads, head_dim // 16), dtype=torch.uint8, device=dev)
@@ -239,7 +245,8 @@ class KVCache:
         self.desc = KVCacheDesc(capacity, heads, head_dim, max_chunks,
                                 self.k_codes.data_ptr(), self.k_scales.data_ptr(),
                                 self.v_codes.data_ptr(), self.v_scales.data_ptr(),
-                                self.gscale.data_ptr(), self.chunk_start.data_ptr(), 0, 0)
+                                self.gscale.data_ptr(), self.chunk_start.data_ptr(), 0, 0,
+                                self.k_center.data_ptr() if self.smooth_k else None)
         check(lib().nvfp4_kv_init(C.byref(self.desc)))
         self.device = dev
         self._ws = None
@@ -252,10 +259,17 @@ class KVCache:
     def n_chunks(self):
         return self.desc.n_chunks
 
+    def _smooth_bytes(self, T: int) -> int:
+        if not self.smooth_k:
+            return 0
+        n = C.c_size_t()
+        check(lib().nvfp4_kv_smooth_workspace(T, self.desc.heads, self.desc.head_dim, C.byref(n)))
+        return n.value
+
     def workspace_bytes(self, T: int) -> int:
         n = C.c_size_t()
         check(lib().nvfp4_kv_append_workspace(T, self.desc.heads, self.desc.head_dim, C.byref(n)))
-        return n.value
+        return n.value + self._smooth_bytes(T)
 
     def append(self, K, V, ws=None, adaptive46=False):
         """Append K, V: bf16 [T, heads, head_dim] tensors, or [T, ld] row views
@@ -288,7 +302,7 @@ class KVCache:
     def qkv_workspace_bytes(self, T: int, D: int) -> int:
         n = C.c_size_t()
         check(lib().nvfp4_qkv_append_workspace(T, self.desc.heads, self.desc.head_dim, D, C.byref(n)))
-        return n.value
+        return n.value + self._smooth_bytes(T)
 
     def qkv_append(self, x, Wq, Ws, Wg, bias=None, out=None, ws=None, adaptive46=False):
         """nvfp4_qkv_append: the QKV projection of x (bf16 [T, D]) with NVFP4

@@ -41,6 +41,7 @@ class KVCacheDesc(C.Structure):
         ("k_codes", _p), ("k_scales", _p), ("v_codes", _p), ("v_scales", _p),
         ("gscale", _p), ("chunk_start", _p),
         ("n_tokens", _i64), ("n_chunks", _i64),
+        ("k_center", _p),
     ]
 
 
@@ -58,6 +59,7 @@ _SIGS = {
                        C.c_int),
     "nvfp4_kv_init": ([C.POINTER(KVCacheDesc)], C.c_int),
     "nvfp4_kv_append_workspace": ([_i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
+    "nvfp4_kv_smooth_workspace": ([_i64, _i64, _i64, C.POINTER(_sz)], C.c_int),
     "nvfp4_kv_append": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _i64, _p, _sz, _p], C.c_int),
     "nvfp4_kv_append_ex": ([C.POINTER(KVCacheDesc), _p, _p, _i64, _i64, C.c_uint32, _p, _sz, _p],
                            C.c_int),

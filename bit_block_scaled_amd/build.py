@@ -26,7 +26,7 @@ LIB = os.path.join(LIBDIR, "libnvfp4.so")
 
 # The GEMM's tile shapes are separate units (the slowest to compile), listed first.
 SOURCES = ["gemm_tile_4x4.hip", "gemm_tile_4x3.hip", "gemm_tile_3x4.hip", "gemm_tile_4x2.hip",
-           "gemm_tile_2x4.hip", "gemm_tile_2x2.hip", "attention.hip", "rht.hip", "quantize.hip", "gemm.hip", "kv.hip", "api.cpp"]
+           "gemm_tile_2x4.hip", "gemm_tile_2x2.hip", "attention.hip", "rht.hip", "quantize.hip", "gemm.hip", "kv.hip", "smooth.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

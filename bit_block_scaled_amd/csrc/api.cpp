@@ -333,6 +333,9 @@ int nvfp4_kv_init(nvfp4_kv_cache *c) {
   if ((s = check_ptr(c->v_scales, "v_scales"))) return s;
   if ((s = check_ptr(c->gscale, "gscale", 8))) return s;
   if ((s = check_ptr(c->chunk_start, "chunk_start", 8))) return s;
+  if (c->k_center != nullptr && (s = check_ptr(c->k_center, "k_center"))) return s;
+  if (c->k_center != nullptr && c->heads * c->head_dim > (int64_t(1) << 20))
+    return fail(NVFP4_EINVAL, "kv_init: K-smoothing needs heads*head_dim <= 2^20");
   c->n_tokens = 0;
   c->n_chunks = 0;
   return NVFP4_OK;
@@ -343,6 +346,41 @@ int nvfp4_kv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t
   if (T < 1 || heads < 1 || head_dim < 32 || head_dim % 32) return fail(NVFP4_EINVAL, "kv_append_workspace: bad geometry");
   *bytes = 2 * kQuantWs;
   return NVFP4_OK;
+}
+
+// Scratch a K-smoothed cache needs after an append's own workspace: the
+// per-strip channel sums, then the smoothed keys [T, e] (no initialisation).
+struct SmoothWs {
+  size_t sums, keys, total;
+};
+static SmoothWs smooth_ws(size_t base, int64_t T, int64_t e) {
+  SmoothWs w;
+  w.sums = round_up(base, 256);
+  w.keys = round_up(w.sums + size_t(nvfp4::smooth_partial_count(T, e)) * sizeof(int64_t), 256);
+  w.total = round_up(w.keys + size_t(T) * size_t(e) * sizeof(uint16_t), 256);
+  return w;
+}
+
+int nvfp4_kv_smooth_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t *bytes) {
+  if (bytes == nullptr) return fail(NVFP4_EINVAL, "bytes is NULL");
+  if (T < 1 || heads < 1 || head_dim < 32 || head_dim % 32) return fail(NVFP4_EINVAL, "kv_smooth_workspace: bad geometry");
+  if (heads * head_dim > (int64_t(1) << 20) || T > kMaxElements / (heads * head_dim))
+    return fail(NVFP4_EINVAL, "kv_smooth_workspace: too large");
+  *bytes = smooth_ws(0, T, heads * head_dim).total;
+  return NVFP4_OK;
+}
+
+// Enqueues the K-smoothing of T keys (token stride ld) of the append about to
+// be made as chunk c->n_chunks; returns the smoothed keys ([T, e], dense).
+static int enqueue_smoothing(const nvfp4_kv_cache *c, const uint16_t *K, int64_t T, int64_t ld,
+                             uint8_t *ws, size_t base, hipStream_t st, const char *who,
+                             const uint16_t **smoothed) {
+  const int64_t e = c->heads * c->head_dim;
+  const SmoothWs w = smooth_ws(base, T, e);
+  nvfp4::SmoothArgs sa{K, T, e, ld, reinterpret_cast<int64_t *>(ws + w.sums), c->k_center + c->n_chunks * e,
+                       reinterpret_cast<uint16_t *>(ws + w.keys)};
+  *smoothed = sa.out;
+  return launched(nvfp4::launch_kv_smooth(sa, st), st, who);
 }
 
 static int check_cache(const nvfp4_kv_cache *c, const char *who) {
@@ -366,19 +404,26 @@ int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, 
   if ((s = check_ptr(V, "V"))) return s;
   if (T > c->capacity - c->n_tokens) return fail(NVFP4_ECAPACITY, "kv_append: token capacity exceeded");
   if (c->n_chunks >= c->max_chunks) return fail(NVFP4_ECAPACITY, "kv_append: no chunk slot left");
-  if (ws == nullptr || ws_bytes < 2 * kQuantWs) return fail(NVFP4_EWORKSPACE, "kv_append: workspace too small");
-  if ((s = check_ptr(ws, "ws"))) return s;
   const int64_t e = c->heads * c->head_dim;           // elements per token
+  const size_t need = c->k_center != nullptr ? smooth_ws(2 * kQuantWs, T, e).total : 2 * kQuantWs;
+  if (ws == nullptr || ws_bytes < need) return fail(NVFP4_EWORKSPACE, "kv_append: workspace too small");
+  if ((s = check_ptr(ws, "ws"))) return s;
   const int64_t off = c->n_tokens * e;
   uint8_t *parts = static_cast<uint8_t *>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint16_t *kin = K;
+  int64_t kld = ld;
+  if (c->k_center != nullptr) {
+    if ((s = enqueue_smoothing(c, K, T, ld, parts, 2 * kQuantWs, st, "kv_append/smooth", &kin))) return s;
+    kld = e;
+  }
   nvfp4::QuantJob jobs[2] = {
-      {K, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T, e, ld},
+      {kin, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T, e, kld},
       {V, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
        parts + kQuantWs, T, e, ld}};
   nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
-  s = launched(nvfp4::launch_quantize(jobs, 2, static_cast<hipStream_t>(stream), &mark,
-                                      (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0),
-               static_cast<hipStream_t>(stream), "kv_append");
+  s = launched(nvfp4::launch_quantize(jobs, 2, st, &mark, (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0), st,
+               "kv_append");
   if (s) return s;
   c->n_tokens += T;
   c->n_chunks += 1;
@@ -432,9 +477,10 @@ int nvfp4_qkv_append(nvfp4_kv_cache *c, const uint16_t *x, int64_t T, int64_t D,
   if ((s = check_ptr(x, "x"))) return s;
   if (T > c->capacity - c->n_tokens) return fail(NVFP4_ECAPACITY, "qkv_append: token capacity exceeded");
   if (c->n_chunks >= c->max_chunks) return fail(NVFP4_ECAPACITY, "qkv_append: no chunk slot left");
+  const QkvWs w = qkv_ws(T, N, D);
+  if (c->k_center != nullptr) need = smooth_ws(w.total, T, hd).total;
   if (ws == nullptr || ws_bytes < need) return fail(NVFP4_EWORKSPACE, "qkv_append: workspace too small");
   if ((s = check_ptr(ws, "ws"))) return s;
-  const QkvWs w = qkv_ws(T, N, D);
   uint8_t *base = static_cast<uint8_t *>(ws);
   uint8_t *aq = base + w.lin.codes;
   uint8_t *as = base + w.lin.scales;
@@ -446,16 +492,24 @@ int nvfp4_qkv_append(nvfp4_kv_cache *c, const uint16_t *x, int64_t T, int64_t D,
   nvfp4::GemmArgs a{aq, as, ag, Wq, Ws, Wg, bias, QKV, T, N, D, 0u};
   int bm = 0, bn = 0;
   nvfp4::gemm_tile_of(a, &bm, &bn);
-  // fused when every tile's columns lie inside one of Q, K, V
-  const bool fused = hd % bn == 0;
+  // fused when every tile's columns lie inside one of Q, K, V (and the keys
+  // are quantised as they are: a K-smoothed cache quantises centred keys,
+  // whose maximum the GEMM tiles do not see)
+  const bool fused = hd % bn == 0 && c->k_center == nullptr;
   if (fused) {
     a.tile_amax = slots;
     if (nvfp4::gemm_tile_count(a) > w.max_tiles) return fail(NVFP4_EHIP, "qkv_append: internal tile count exceeds the workspace");
   }
   if ((s = launched(nvfp4::launch_gemm(a, st), st, "qkv_append/gemm"))) return s;
   const int64_t off = c->n_tokens * hd;
+  const uint16_t *kin = QKV + hd;
+  int64_t kld = N;
+  if (c->k_center != nullptr) {
+    if ((s = enqueue_smoothing(c, QKV + hd, T, N, base, w.total, st, "qkv_append/smooth", &kin))) return s;
+    kld = hd;
+  }
   nvfp4::QuantJob jobs[2] = {
-      {QKV + hd, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, base + w.app, T, hd, N},
+      {kin, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, base + w.app, T, hd, kld},
       {QKV + 2 * hd, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
        base + w.app + kQuantWs, T, hd, N}};
   const nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
@@ -494,6 +548,7 @@ int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1, uint16_t *
   a.t0 = t0;
   a.t1 = t1;
   a.elems_per_token = c->heads * c->head_dim;
+  a.kcenter = c->k_center;
   return launched(nvfp4::launch_kv_dequant(a, static_cast<hipStream_t>(stream)),
                   static_cast<hipStream_t>(stream), "kv_dequant");
 }
@@ -621,6 +676,7 @@ int nvfp4_kv_attention(const nvfp4_kv_cache *c, const uint16_t *Q, int64_t Tq, i
   a.gscale = c->gscale;
   a.chunk_start = c->chunk_start;
   a.n_chunks = c->n_chunks;
+  a.kcenter = c->k_center;
   return run_attention(a, false, scale, ws, ws_bytes, stream, "kv_attention");
 }
 

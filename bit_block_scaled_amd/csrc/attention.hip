@@ -60,11 +60,14 @@ struct alignas(16) AttnTile {     // 16-byte multiple: both buffers keep 16-byte
   uint8_t k[kAK * kKRow];
   uint8_t v[kAD * kVRow];
   float gk[kAK], gv[kAK];     // per key: g_K·scale·log2(e) and g_V (0 past the keys)
+  int32_t ck[kAK];            // K-smoothing: per key the append index (−1 past the keys)
+  int32_t uni, pad_[3];       // K-smoothing: the append of every key of the tile, or −1
 };
 static_assert(sizeof(AttnTile) % 16 == 0, "tile buffers must stay 16-byte aligned");
 struct AttnLds {
   AttnTile buf[2];
   int32_t starts[kAttnLdsStarts];
+  float bq[kAThreads];        // K-smoothing: each thread's q·μ of append `cb`
 };
 
 // The append that the previous key of this thread's slot belonged to, with
@@ -73,6 +76,7 @@ struct AttnLds {
 struct ChunkCache {
   int32_t lo = 0, hi = 0;
   float gk = 0.0f, gv = 0.0f;
+  int32_t ci = -1;
 };
 
 // Token of virtual key j (the concatenated ranges), or -1 past the keys.
@@ -217,7 +221,7 @@ __device__ __forceinline__ void attn_decode8_f32(uint32_t w, float s, float (&o)
 }
 
 // Writes one fetched tile into LDS (K rows, Vᵀ rows, per-key factors).
-template <bool BF16>
+template <bool BF16, bool SMOOTH>
 __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, const int32_t *lds_starts,
                                            ChunkCache &cc, const AttnArgs &a) {
   const int t = threadIdx.x;
@@ -272,6 +276,7 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, c
           cc.hi = lds_starts != nullptr ? lds_starts[ci + 1] : (int32_t)a.chunk_start[ci + 1];
           cc.gk = a.gscale[2 * ci] * a.qk_scale;
           cc.gv = a.gscale[2 * ci + 1];
+          cc.ci = (int32_t)ci;
         }
         gk = cc.gk;
         gv = cc.gv;
@@ -282,11 +287,50 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, c
     }
     L.gk[t] = gk;
     L.gv[t] = gv;
+    if constexpr (SMOOTH) {
+      // wave 0 (keys 0..63): the append of each key, and whether one append
+      // holds every key of the tile (key 0 always exists)
+      const int32_t ck = f.tok >= 0 ? cc.ci : -1;
+      L.ck[t] = ck;
+      const int32_t ck0 = __shfl(ck, 0, 64);
+      const uint64_t others = __ballot(f.tok >= 0 && ck != ck0);     // the whole wave votes
+      if (t == 0) L.uni = others == 0 ? ck0 : -1;
+    }
   }
 }
 
-template <bool BF16>
+// K-smoothing: q·μ of this lane's query (row q of Q) and the centre row of
+// append c, in units of the scaled scores (times scale·log2(e)).  Each
+// half-wave covers half of the dimensions (d = 16·st + 8·hh .. +7), from the
+// bf16 query in memory (bf16 products are exact in the fp32 dot); one
+// exchange adds the halves.  One 16-byte segment of each row in registers at
+// a time: this runs while the tile loop holds its full register set.
+__device__ __forceinline__ float attn_center_dot(const AttnArgs &a, int64_t q, int h, int hh, int32_t c) {
+  const uint16_t *mr = a.kcenter + ((int64_t)c * a.heads + h) * kAD + 8 * hh;
+  const uint16_t *qr = a.q + q * a.ldq + (int64_t)h * kAD + 8 * hh;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    // 8 bytes of each row at a time; the pairs taken with shuffles of the
+    // 4-element vectors (a bit cast of each 32-bit element to a bf16 pair
+    // was compiled to read element 0 every time)
+    const int off = 16 * (i >> 1) + 4 * (i & 1);
+    const bf16x4 mv = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(mr + off));
+    const bf16x4 qv = __builtin_bit_cast(bf16x4, *reinterpret_cast<const u32x2 *>(qr + off));
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 0, 1), __builtin_shufflevector(mv, mv, 0, 1),
+                                           acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(qv, qv, 2, 3), __builtin_shufflevector(mv, mv, 2, 3),
+                                           acc, false);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  acc += __shfl_xor(acc, 32, 64);
+  return acc * a.qk_scale;
+}
+
+template <bool BF16, bool SMOOTH>
 __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
+  static_assert(!(BF16 && SMOOTH), "K-smoothing applies to the NVFP4 cache only");
   __shared__ __attribute__((aligned(16))) AttnLds L;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 31, hh = lane >> 5;
@@ -327,6 +371,7 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
   }
 
   float m = -__builtin_huge_valf(), l = 0.0f;
+  int32_t cb = -1;          // K-smoothing: the append whose q·μ is in L.bq
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -340,7 +385,7 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
   if constexpr (!BF16) {
     if (starts_in_lds) __syncthreads();
   }
-  tile_store<BF16>(fin, L.buf[0], lds_starts, cc, a);
+  tile_store<BF16, SMOOTH>(fin, L.buf[0], lds_starts, cc, a);
   __syncthreads();
   if (j0 + kAK < j1) tile_fetch<BF16>(fin, a, h, j0 + kAK, j1);
   int cur = 0;
@@ -348,11 +393,23 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
     // decode the next tile into the other buffer (its loads were issued one
     // tile ago), then fetch the one after it
     if (jt + kAK < j1) {
-      tile_store<BF16>(fin, L.buf[cur ^ 1], lds_starts, cc, a);
+      tile_store<BF16, SMOOTH>(fin, L.buf[cur ^ 1], lds_starts, cc, a);
       if (jt + 2 * kAK < j1) tile_fetch<BF16>(fin, a, h, jt + 2 * kAK, j1);
     }
     const AttnTile &B = L.buf[cur];
 
+    // Keys of a smoothed cache are E2M1·S·g + μ: each score gains q·μ of its
+    // key's append.  A tile inside one append (the usual case) needs one
+    // value per query, found here before the score registers are in use and
+    // kept for the next tiles; a tile over several appends adds the value of
+    // each run of keys after the products (below).
+    if constexpr (SMOOTH) {
+      const int32_t uni = __builtin_amdgcn_readfirstlane(B.uni);
+      if (uni >= 0 && uni != cb) {
+        L.bq[threadIdx.x] = attn_center_dot(a, qc, h, hh, uni);
+        cb = uni;
+      }
+    }
     // Sᵀ = K·Qᵀ: lane (query r, hh) gets keys 32kb + 8(v/4) + 4hh + v%4
     f32x16 s[2];
 #pragma unroll
@@ -377,7 +434,63 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
     // score −inf.
     const int kvalid = (j1 - jt) < kAK ? (int)(j1 - jt) : kAK;
     float mt = -__builtin_huge_valf();
-    if (kvalid == kAK) {
+    if constexpr (SMOOTH) {
+      if (B.uni >= 0) {
+        // one append holds the tile: the term q·μ of the scaled score
+        const float bq = L.bq[threadIdx.x];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int key0 = 32 * kb + 8 * g4 + 4 * hh;
+            const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[key0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float tv = key0 + e < kvalid ? __builtin_fmaf(s[kb][4 * g4 + e], gk4[e], bq)
+                                                 : -__builtin_huge_valf();
+              s[kb][4 * g4 + e] = tv;
+              mt = __builtin_fmaxf(mt, tv);
+            }
+          }
+      } else {
+        const int32_t ckl = B.ck[lane];
+        uint64_t runs = __ballot(lane == 0 || ckl != B.ck[lane == 0 ? 0 : lane - 1]);
+        while (runs != 0) {
+          const int k0 = __builtin_ctzll(runs);
+          runs &= runs - 1;
+          const int k1 = runs != 0 ? __builtin_ctzll(runs) : kAK;
+          const int32_t c = __builtin_amdgcn_readfirstlane(B.ck[k0]);
+          if (c < 0) continue;                       // keys past the end (masked below)
+          if (c != cb) {
+            L.bq[threadIdx.x] = attn_center_dot(a, qc, h, hh, c);
+            cb = c;
+          }
+          const float bi = L.bq[threadIdx.x] / B.gk[k0];   // enters before the key factor
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int key = 32 * kb + 8 * g4 + 4 * hh + e;
+                if (key >= k0 && key < k1) s[kb][4 * g4 + e] += bi;
+              }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int key0 = 32 * kb + 8 * g4 + 4 * hh;
+            const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[key0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float tv = key0 + e < kvalid ? s[kb][4 * g4 + e] * gk4[e] : -__builtin_huge_valf();
+              s[kb][4 * g4 + e] = tv;
+              mt = __builtin_fmaxf(mt, tv);
+            }
+          }
+      }
+    } else if (kvalid == kAK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -544,9 +657,11 @@ int64_t attention_keys_per_split(int64_t Tk, int64_t nsplit) {
 hipError_t launch_attention(const AttnArgs &a, bool bf16, hipStream_t stream) {
   const dim3 grid((unsigned)((a.Tq + kAQ - 1) / kAQ), (unsigned)a.heads, (unsigned)a.nsplit);
   if (bf16)
-    hipLaunchKernelGGL(k_attention<true>, grid, dim3(kAThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_attention<true, false>), grid, dim3(kAThreads), 0, stream, a);
+  else if (a.kcenter != nullptr)
+    hipLaunchKernelGGL((k_attention<false, true>), grid, dim3(kAThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_attention<false>, grid, dim3(kAThreads), 0, stream, a);
+    hipLaunchKernelGGL((k_attention<false, false>), grid, dim3(kAThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.part_o == nullptr) return e;
   const int64_t rows = a.Tq * a.heads;

@@ -111,9 +111,24 @@ struct KvDequantArgs {
   int64_t n_chunks;
   int64_t t0, t1;
   int64_t elems_per_token;      // heads · head_dim (multiple of 32)
+  const uint16_t *kcenter;      // K-smoothing: bf16 [chunks, elems_per_token] centres, or null
 };
 
 hipError_t launch_kv_dequant(const KvDequantArgs &a, hipStream_t stream);
+
+// K-smoothing of one appended chunk: keys k [T, e] bf16 (token t at k + t·ld,
+// e and ld multiples of 8, 16-byte aligned), the channel centres written to
+// center [e] (bf16), the smoothed keys to out [T, e] (dense).  partials holds
+// smooth_partial_count(T, e) 64-bit integers, written before they are read.
+struct SmoothArgs {
+  const uint16_t *k;
+  int64_t T, e, ld;
+  int64_t *partials;
+  uint16_t *center;
+  uint16_t *out;
+};
+int64_t smooth_partial_count(int64_t T, int64_t e);
+hipError_t launch_kv_smooth(const SmoothArgs &a, hipStream_t stream);
 
 // Attention of bf16 queries over keys/values from the NVFP4 cache (or, for the
 // bf16 twin, from bf16 K/V tensors).  head_dim is 128.  Keys are the tokens of
@@ -140,6 +155,7 @@ struct AttnArgs {
   int n_ranges;
   int64_t Tk;
   float qk_scale;               // scale · log2(e)
+  const uint16_t *kcenter;      // K-smoothing: bf16 [chunks, heads·128] centres, or null
   int nsplit;
   int64_t keys_per_split;
   float *part_o, *part_ml;

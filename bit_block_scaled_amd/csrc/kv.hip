@@ -9,7 +9,8 @@
 // load and store instruction of a wave covers consecutive memory; a thread
 // handles kKvU groups, kKvThreads apart.  out = bf16(fl32(fl32(E2M1·S)·g)),
 // where g is the tensor scale of the append that wrote the token (the E2M1·S
-// product is exact in binary32).
+// product is exact in binary32); keys of a K-smoothed cache get their
+// append's channel centre added in binary32 before the bf16 rounding.
 //
 // Finding each token's append: a wave covers few tokens (under 3 for 24
 // heads of 128), so it first brackets its token range: the appends holding
@@ -68,6 +69,26 @@ __device__ __forceinline__ u32x4 dequant_dword(uint32_t w, float s, float g) {
   return o;
 }
 
+// Keys of a K-smoothed cache: the same chain, then the append's channel
+// centre added in binary32 (a separate rounding, never fused with the
+// product) before the bf16 rounding.
+template <int SEL>
+__device__ __forceinline__ uint32_t dequant_pair_centred(uint32_t w, float s, float g, uint32_t mu2) {
+#pragma clang fp contract(off)
+  const f32x2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  const float a = (e.x * s) * g, b = (e.y * s) * g;
+  return pack_bf16x2(a + bf16_bits_to_f32(mu2 & 0xFFFFu), b + bf16_bits_to_f32(mu2 >> 16));
+}
+
+__device__ __forceinline__ u32x4 dequant_dword_centred(uint32_t w, float s, float g, const u32x4 &mu) {
+  u32x4 o;
+  o.x = dequant_pair_centred<0>(w, s, g, mu.x);
+  o.y = dequant_pair_centred<1>(w, s, g, mu.y);
+  o.z = dequant_pair_centred<2>(w, s, g, mu.z);
+  o.w = dequant_pair_centred<3>(w, s, g, mu.w);
+  return o;
+}
+
 __global__ void __launch_bounds__(kKvThreads) k_kv_dequant(KvDequantArgs a) {
   const int which = blockIdx.y;
   const int64_t e = a.elems_per_token;
@@ -102,7 +123,14 @@ __global__ void __launch_bounds__(kKvThreads) k_kv_dequant(KvDequantArgs a) {
     if (q[i] >= groups) continue;
     const int64_t ci = c_lo == c_hi ? c_lo : chunk_in(a.chunk_start, c_lo, c_hi, token(q[i]));
     const float g = a.gscale[2 * ci + which];
-    const u32x4 o = dequant_dword(c[i], e4m3_decode(sb[i]), g);
+    u32x4 o;
+    if (which == 0 && a.kcenter != nullptr) {
+      const int64_t ch = 8 * q[i] - (token(q[i]) - a.t0) * e;        // channel of the group
+      const u32x4 mu = *reinterpret_cast<const u32x4 *>(a.kcenter + ci * e + ch);
+      o = dequant_dword_centred(c[i], e4m3_decode(sb[i]), g, mu);
+    } else {
+      o = dequant_dword(c[i], e4m3_decode(sb[i]), g);
+    }
     // non-temporal: the output streams past L2 and the MALL
     __builtin_nontemporal_store(o, &out[q[i]]);
   }

@@ -1,0 +1,149 @@
+// K-smoothing of an appended KV chunk (gfx950): the per-channel centre of the
+// chunk's keys and the smoothed keys that are then quantised.
+//
+// Source: "LongLive-2.0：用 NVFP4 并行底座做长视频生成", 二、方法 / 推理底座 (each
+// KV chunk is quantised again on its own, with K-smoothing on its keys).  The
+// pages name K-smoothing without defining it; the definition used here:
+//   centre of channel c over the chunk's T tokens
+//     z_t = clamp(round_half_even(K[t, c] · 2^24), −2^38, 2^38)
+//     S   = Σ_t z_t                     (exact, 64-bit integers, any order)
+//     μ_c = bf16_rne(fl64(fl64(S) / T) · 2^-24)
+//   smoothed key K'[t, c] = bf16_rne(fl32(K[t, c] − μ_c)).
+// Because the sum is exact integer arithmetic, the centre does not depend on
+// the order in which the parts are added.  The workspace needs no
+// initialisation: every partial sum is written before it is read.
+//
+// Three launches, each a plain HBM stream:
+//   k_kv_colsum  — workgroups own 128 tokens x 512 channels; every lane sums 8
+//                  channels over 32 tokens (16-byte loads along the channels),
+//                  the four token rows of a workgroup meet in LDS, and the
+//                  workgroup stores its 128-token partial sum of each channel;
+//   k_kv_center  — one thread per channel adds the partial sums of all token
+//                  strips, turns the sum into μ and writes it to the cache's
+//                  centre row of this append;
+//   k_kv_smooth_apply — K' into the workspace, 8 channels per lane.
+// The quantiser then encodes K' (and V) as for an unsmoothed append.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+
+constexpr int kSmThreads = 256;
+constexpr int kSmChan = 512;              // channels per colsum workgroup (64 lanes x 8)
+constexpr int kSmRows = kSmThreads / 64;  // token rows per colsum workgroup
+constexpr int kSmPerRow = 32;             // tokens per row
+constexpr int kSmStrip = kSmRows * kSmPerRow;
+
+// The key's count of 2^-24 steps, nearest-even, saturated at ±2^38 (exact in
+// binary64: a bf16 times 2^24 needs 8 significant bits).
+__device__ __forceinline__ int64_t grid_steps(uint32_t bf16) {
+  double d = (double)bf16_bits_to_f32(bf16) * 16777216.0;
+  d = __builtin_rint(d);
+  d = d < -274877906944.0 ? -274877906944.0 : (d > 274877906944.0 ? 274877906944.0 : d);
+  return (int64_t)d;
+}
+
+__global__ void __launch_bounds__(kSmThreads) k_kv_colsum(SmoothArgs a) {
+  __shared__ int64_t red[kSmRows][64][8];
+  const int lane = threadIdx.x & 63, row = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.y * kSmChan + 8 * lane;
+  const int64_t t0 = (int64_t)blockIdx.x * kSmStrip + row;
+  int64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c0 < a.e) {
+#pragma unroll 4
+    for (int i = 0; i < kSmPerRow; ++i) {
+      const int64_t t = t0 + (int64_t)kSmRows * i;
+      if (t < a.T) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.k + t * a.ld + c0);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += grid_steps(w[k] & 0xFFFFu);
+          acc[2 * k + 1] += grid_steps(w[k] >> 16);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) red[row][lane][k] = acc[k];
+  __syncthreads();
+  // thread j adds channels 2j and 2j + 1 of the workgroup's 512 and stores
+  // the strip's partial sums
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ch = 2 * threadIdx.x + h;
+    const int64_t c = (int64_t)blockIdx.y * kSmChan + ch;
+    if (c < a.e) {
+      int64_t s = 0;
+#pragma unroll
+      for (int r = 0; r < kSmRows; ++r) s += red[r][ch >> 3][ch & 7];
+      a.partials[(int64_t)blockIdx.x * a.e + c] = s;
+    }
+  }
+}
+
+// Nearest-even bf16 of a binary64 value in the centre's range: 0 or a
+// magnitude in [2^-48, 2^14] (a normal bf16): 7 of the 52 fraction bits kept.
+__device__ __forceinline__ uint16_t bf16_rne_from_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t sign = (uint32_t)(b >> 63) << 15;
+  const uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+  if (mag == 0) return (uint16_t)sign;
+  uint32_t exp = (uint32_t)(mag >> 52) - 1023u + 127u;
+  uint64_t keep = (mag & 0xFFFFFFFFFFFFFull) >> 45;
+  const uint64_t rem = mag & ((uint64_t(1) << 45) - 1), half = uint64_t(1) << 44;
+  if (rem > half || (rem == half && (keep & 1u))) ++keep;
+  if (keep == 128) {
+    keep = 0;
+    ++exp;
+  }
+  return (uint16_t)(sign | (exp << 7) | (uint32_t)keep);
+}
+
+__global__ void __launch_bounds__(kSmThreads) k_kv_center(SmoothArgs a) {
+  const int64_t c = (int64_t)blockIdx.x * kSmThreads + threadIdx.x;
+  if (c >= a.e) return;
+  const int64_t strips = (a.T + kSmStrip - 1) / kSmStrip;
+  int64_t S = 0;                                   // exact: |S| <= 2^62
+  for (int64_t p = 0; p < strips; ++p) S += a.partials[p * a.e + c];
+  const double mean = (double)S / (double)a.T;
+  a.center[c] = bf16_rne_from_f64(mean * 0x1p-24);
+}
+
+__global__ void __launch_bounds__(kSmThreads) k_kv_smooth_apply(SmoothArgs a) {
+  const int64_t per_tok = a.e / 8;
+  const int64_t g = (int64_t)blockIdx.x * kSmThreads + threadIdx.x;
+  if (g >= a.T * per_tok) return;
+  const int64_t t = g / per_tok, c = 8 * (g - t * per_tok);
+  const u32x4 v = *reinterpret_cast<const u32x4 *>(a.k + t * a.ld + c);
+  const u32x4 m = *reinterpret_cast<const u32x4 *>(a.center + c);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w}, mu[4] = {m.x, m.y, m.z, m.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float lo = bf16_bits_to_f32(w[k] & 0xFFFFu) - bf16_bits_to_f32(mu[k] & 0xFFFFu);
+    const float hi = bf16_bits_to_f32(w[k] >> 16) - bf16_bits_to_f32(mu[k] >> 16);
+    o[k] = pack_bf16x2(lo, hi);
+  }
+  *reinterpret_cast<u32x4 *>(a.out + t * a.e + c) = u32x4{o[0], o[1], o[2], o[3]};
+}
+
+int64_t smooth_partial_count(int64_t T, int64_t e) { return (T + kSmStrip - 1) / kSmStrip * e; }
+
+hipError_t launch_kv_smooth(const SmoothArgs &a, hipStream_t stream) {
+  if (a.T < 1 || a.e < 8 || a.e % 8) return hipErrorInvalidValue;
+  const int64_t strips = (a.T + kSmStrip - 1) / kSmStrip, cgroups = (a.e + kSmChan - 1) / kSmChan;
+  const int64_t groups = a.T * (a.e / 8);
+  const int64_t apply_blocks = (groups + kSmThreads - 1) / kSmThreads;
+  if (strips > 0x7FFFFFFF || cgroups > 65535 || apply_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_kv_colsum, dim3((unsigned)strips, (unsigned)cgroups), dim3(kSmThreads), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_kv_center, dim3((unsigned)((a.e + kSmThreads - 1) / kSmThreads)), dim3(kSmThreads), 0,
+                     stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_kv_smooth_apply, dim3((unsigned)apply_blocks), dim3(kSmThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -235,6 +235,16 @@ int nvfp4_linear(const uint16_t *x,
  * append quantises K and V (each viewed as [T·H, head_dim], blocks of 16
  * along head_dim) with its own pair of tensor scales and writes them at token
  * offset n_tokens.
+ *
+ * K-smoothing (二、方法 / 推理底座 names it for the keys of each KV chunk and
+ * does not define it; the definition used): when k_center is not NULL, every
+ * append first takes the centre of each key channel over its T tokens,
+ *     μ = bf16_rne( fl64( fl64(Σ_t clamp(rne(K·2^24), ±2^38)) / T ) · 2^-24 )
+ * (an exact integer sum on a 2^-24 grid, so the result does not depend on
+ * summation order), stores it as row n_chunks of k_center, and quantises the
+ * smoothed keys bf16_rne(fl32(K − μ)) in place of K.  Read-back and attention
+ * add μ back (see nvfp4_kv_dequant, nvfp4_kv_attention).  V is not smoothed.
+ * The choice is made once, at nvfp4_kv_init, for every append of the cache.
  */
 typedef struct nvfp4_kv_cache {
     int64_t capacity;      /* tokens the buffers hold                        */
@@ -249,6 +259,9 @@ typedef struct nvfp4_kv_cache {
     int64_t *chunk_start;  /* device [max_chunks + 1]: first token per chunk */
     int64_t n_tokens;      /* host counter: tokens written                   */
     int64_t n_chunks;      /* host counter: appends made                     */
+    uint16_t *k_center;    /* device [max_chunks, heads, head_dim] bf16 key
+                              centres (16-byte aligned), or NULL: no
+                              K-smoothing.  Requires heads·head_dim <= 2^20. */
 } nvfp4_kv_cache;
 
 /* Validate geometry and pointers, zero the counters.  Enqueues nothing. */
@@ -256,6 +269,12 @@ int nvfp4_kv_init(nvfp4_kv_cache *c);
 
 /* Workspace bytes nvfp4_kv_append needs for an append of T tokens. */
 int nvfp4_kv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t *bytes);
+
+/* Extra workspace bytes an append of T tokens to a K-smoothed cache needs,
+ * placed after the workspace of nvfp4_kv_append (or nvfp4_qkv_append): the
+ * channel sums of each 128-token strip and the smoothed keys.  This part
+ * needs no initialisation. */
+int nvfp4_kv_smooth_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t *bytes);
 
 /*
  * Quantise K and V (bf16, T tokens of [heads, head_dim]) into the cache at
@@ -310,8 +329,10 @@ int nvfp4_qkv_append(nvfp4_kv_cache *c, const uint16_t *x, int64_t T, int64_t D,
  * Dequantise tokens [t0, t1) of K and V to bf16 [t1-t0, heads, head_dim]:
  *   out = bf16( fl32( fl32(E2M1 · E4M3) · g_chunk ) )
  * (the first product is exact; g_chunk is the tensor scale of the append that
- * wrote the token).  Requires 0 <= t0 <= t1 <= c->n_tokens; t0 == t1 is a no-op
- * (the output pointers are then not used and may be NULL).
+ * wrote the token); keys of a K-smoothed cache are
+ *   bf16( fl32( fl32( fl32(E2M1 · E4M3) · g_chunk ) + μ_chunk ) ).
+ * Requires 0 <= t0 <= t1 <= c->n_tokens; t0 == t1 is a no-op (the output
+ * pointers are then not used and may be NULL).
  */
 int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1,
                      uint16_t *K_out, uint16_t *V_out, void *stream);
@@ -325,7 +346,9 @@ int nvfp4_kv_dequant(const nvfp4_kv_cache *c, int64_t t0, int64_t t1,
  * without duplicates).  For each head h and query i:
  *   O[i, h] = softmax_j( Q[i, h] · K[j, h] · scale ) · V[j, h]
  * over the tokens j of `ranges`, with K and V the exact dequantised values
- * E2M1 · E4M3 · g of each token's append.
+ * E2M1 · E4M3 · g of each token's append (keys of a K-smoothed cache:
+ * E2M1 · E4M3 · g + μ, the append's centre; each score then gains Q·μ,
+ * computed in fp32 from the fp16 query, once per query and append).
  *   c        cache with head_dim 128 (others: NVFP4_EINVAL)
  *   Q        bf16: query i, head h at Q + i·ldq + 128·h (ldq >= heads·128,
  *            ldq % 8 == 0; Q may be the query slice of a fused QKV output)

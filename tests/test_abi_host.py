@@ -158,6 +158,31 @@ def test_kv_append_capacity_and_args(L):
     assert L.nvfp4_kv_append(C.byref(_desc(n_tokens=500)), FAKE, FAKE, 1, 3072, ws, wsb, None) == EINVAL
 
 
+def test_kv_smoothing_host_checks(L):
+    # the centre table is optional (NULL: no K-smoothing) and must be aligned
+    assert L.nvfp4_kv_init(C.byref(_desc(k_center=MIS))) == EINVAL
+    assert L.nvfp4_kv_init(C.byref(_desc(k_center=None))) == 0
+    d = _desc(k_center=FAKE)
+    assert L.nvfp4_kv_init(C.byref(d)) == 0
+    n, m = C.c_size_t(), C.c_size_t()
+    assert L.nvfp4_kv_append_workspace(880, 24, 128, C.byref(n)) == 0
+    assert L.nvfp4_kv_smooth_workspace(880, 24, 128, C.byref(m)) == 0
+    assert m.value >= 880 * 3072 * 2 + 3072 * 8                    # smoothed keys + channel sums
+    assert L.nvfp4_kv_smooth_workspace(880, 24, 100, C.byref(m)) == EINVAL
+    assert L.nvfp4_kv_smooth_workspace(0, 24, 128, C.byref(m)) == EINVAL
+    assert L.nvfp4_kv_smooth_workspace(880, 24, 128, None) == EINVAL
+    # an append to a smoothed cache needs both parts; with only the plain
+    # workspace it is refused before anything is enqueued
+    assert L.nvfp4_kv_append_workspace(10, 24, 128, C.byref(n)) == 0
+    assert L.nvfp4_kv_append(C.byref(d), FAKE, FAKE, 10, 3072, FAKE, n.value, None) == EWS
+    assert d.n_tokens == 0 and d.n_chunks == 0
+    need = C.c_size_t()
+    assert L.nvfp4_qkv_append_workspace(10, 24, 128, 3072, C.byref(need)) == 0
+    assert L.nvfp4_qkv_append(C.byref(d), FAKE, 10, 3072, FAKE, FAKE, FAKE, None, FAKE, 0, FAKE,
+                              need.value, None) == EWS
+    assert d.n_tokens == 0 and d.n_chunks == 0
+
+
 def test_kv_dequant_range(L):
     d = _desc()
     assert L.nvfp4_kv_init(C.byref(d)) == 0
