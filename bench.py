@@ -22,8 +22,9 @@ gives the per-kernel breakdown and the dominant kernel's roofline (the up
 GEMM).  Further entries in `kernels` time the other configurations' kernels
 (QKV and long-context GEMMs and quantisers, an 880-token frame step of QKV
 projection + KV append with the append fused into the projection or not, the
-65536-token KV append sequence and its read-back, attention of an 880-token query chunk over that
-cache read in NVFP4 against the same kernel on bf16 K/V, the FFN up
+65536-token KV append sequence and its read-back, the same cache in 8-frame chunks with adaptive
+scales, with and without K-smoothing, attention of an 880-token query chunk over that
+cache read in NVFP4 (plain and K-smoothed) against the same kernel on bf16 K/V, the FFN up
 projection's weight gradient with Hadamard-transformed operands, a 1 GiB
 device copy) with p10/p50/p90 over repetitions; the HBM-bound ones after a
 1 GiB cache flush ("cold").
@@ -525,7 +526,32 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
     kernels["kv65536_append_8frame_chunks_cold"] = {"appends": len(sizes8), "tokens": T, "us": pct(t),
                                                     "roofline": roof_hbm(2 * T * 3072 * Q_BYTES_PER_ELEM + 8 * len(sizes8),
                                                                          float(np.median(t)))}
-    del cache8
+    # the pages' KV configuration: 8-frame chunks with adaptive {4, 6} scales,
+    # without and with K-smoothing (the smoothed append adds three passes:
+    # channel sums, centres, smoothed keys; the roofline counts only the
+    # append's own bytes, so it shows what smoothing costs)
+    cache8s = nv.KVCache(T, 24, 128, max_chunks=len(sizes8), device=dev, smooth_k=True)
+    for name, c8 in (("adaptive", cache8), ("smoothed_adaptive", cache8s)):
+        def seq8a(c8=c8):
+            c8.reset()
+            for i in range(len(sizes8)):
+                c8.append(kd[starts8[i]:starts8[i + 1]], vd[starts8[i]:starts8[i + 1]], adaptive46=True)
+        t = time_us(torch, seq8a, 10, 2, flush)
+        kernels[f"kv65536_append_8frame_chunks_{name}_cold"] = {
+            "appends": len(sizes8), "tokens": T, "us": pct(t),
+            "roofline": roof_hbm(2 * T * 3072 * Q_BYTES_PER_ELEM + 8 * len(sizes8), float(np.median(t)))}
+    del cache8, cache8s
+    # 880-token appends with K-smoothing (the frame-by-frame cache), kept for
+    # the attention comparison below
+    cache_s = nv.KVCache(T, 24, 128, max_chunks=len(sizes), device=dev, smooth_k=True)
+
+    def seq_s():
+        cache_s.reset()
+        for i in range(len(sizes)):
+            cache_s.append(kd[starts[i]:starts[i + 1]], vd[starts[i]:starts[i + 1]])
+    t = time_us(torch, seq_s, 10, 2, flush)
+    kernels["kv65536_append_sequence_smoothed_cold"] = {"appends": len(sizes), "tokens": T, "us": pct(t),
+                                                        "roofline": roof_hbm(kvb, float(np.median(t)))}
     # each 880-token append inside the back-to-back sequence: an event after
     # every append, per-append time = the gap between consecutive events
     per = []
@@ -561,6 +587,7 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
         ws_a = nv._attention_ws(880, 24, Tk, dev)
         flops_a = 4.0 * 880 * Tk * 24 * 128
         tn = time_us(torch, lambda: cache.attention(qa, ranges, out=oa, ws=ws_a), 10, 3)
+        ts = time_us(torch, lambda: cache_s.attention(qa, ranges, out=oa, ws=ws_a), 10, 3)
         if name == "full":
             kb, vb = ko, vo
         else:
@@ -578,13 +605,16 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
         pn, pb, pu = float(np.median(tn)), float(np.median(tb)), float(np.median(tu))
         kernels[f"attention_{name}_nvfp4"] = {"queries": 880, "keys": Tk, "heads": 24, "us": pct(tn),
                                              "roofline": roof_gemm(flops_a, pn)}
+        kernels[f"attention_{name}_nvfp4_smoothed"] = {"queries": 880, "keys": Tk, "heads": 24, "us": pct(ts),
+                                                      "time_ratio_vs_nvfp4": round(float(np.median(ts)) / pn, 4),
+                                                      "roofline": roof_gemm(flops_a, float(np.median(ts)))}
         kernels[f"attention_{name}_bf16_twin"] = {"queries": 880, "keys": Tk, "heads": 24, "us": pct(tb),
                                                  "roofline": roof_gemm(flops_a, pb)}
         kernels[f"attention_{name}_dequant_then_bf16"] = {"us": pct(tu)}
         kernels[f"attention_{name}_nvfp4_vs_bf16"] = {"time_ratio": round(pn / pb, 4),
                                                        "dequant_then_bf16_ratio": round(pu / pb, 4)}
         del ws_a
-    del cache, ko, vo, qa, oa
+    del cache, cache_s, ko, vo, qa, oa
     torch.cuda.empty_cache()
 
     wgrad_leg(kernels, nv, torch, np, workloads, dev, up, flush)

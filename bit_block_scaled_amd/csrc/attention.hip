@@ -55,20 +55,35 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
 // One decoded key tile.  The workgroup keeps two: it decodes tile i+1 into
 // one while its waves read tile i from the other, so one barrier per tile
-// orders both.
+// orders both.  A K-smoothed cache adds per-key append indices and the
+// centre row of the tile's last append.
+template <bool SMOOTH>
 struct alignas(16) AttnTile {     // 16-byte multiple: both buffers keep 16-byte rows aligned
   uint8_t k[kAK * kKRow];
   uint8_t v[kAD * kVRow];
   float gk[kAK], gv[kAK];     // per key: g_K·scale·log2(e) and g_V (0 past the keys)
-  int32_t ck[kAK];            // K-smoothing: per key the append index (−1 past the keys)
-  int32_t uni, pad_[3];       // K-smoothing: the append of every key of the tile, or −1
 };
-static_assert(sizeof(AttnTile) % 16 == 0, "tile buffers must stay 16-byte aligned");
+template <>
+struct alignas(16) AttnTile<true> {
+  uint8_t k[kAK * kKRow];
+  uint8_t v[kAD * kVRow];
+  float gk[kAK], gv[kAK];
+  int32_t ck[kAK];              // per key the append index (−1 past the keys)
+};
+static_assert(sizeof(AttnTile<false>) % 16 == 0 && sizeof(AttnTile<true>) % 16 == 0,
+              "tile buffers must stay 16-byte aligned");
+// Chunk starts kept in LDS (as int32): fewer with K-smoothing, whose larger
+// tiles and q·μ slots must leave two workgroups per CU.
+template <bool SMOOTH>
+constexpr int attn_lds_starts() { return SMOOTH ? 1984 : kAttnLdsStarts; }
+template <bool SMOOTH>
 struct AttnLds {
-  AttnTile buf[2];
-  int32_t starts[kAttnLdsStarts];
-  float bq[kAThreads];        // K-smoothing: each thread's q·μ of append `cb`
+  AttnTile<SMOOTH> buf[2];
+  int32_t starts[attn_lds_starts<SMOOTH>()];
+  float bq[SMOOTH ? 2 : 1][SMOOTH ? kAThreads : 1];   // K-smoothing: two q·μ slots per thread
 };
+static_assert(2 * sizeof(AttnLds<true>) <= 160 * 1024 && 2 * sizeof(AttnLds<false>) <= 160 * 1024,
+              "two workgroups per CU");
 
 // The append that the previous key of this thread's slot belonged to, with
 // its factors: consecutive tiles move each slot's token forward by 64, so the
@@ -76,7 +91,7 @@ struct AttnLds {
 struct ChunkCache {
   int32_t lo = 0, hi = 0;
   float gk = 0.0f, gv = 0.0f;
-  int32_t ci = -1;
+  int32_t ci = -1;              // K-smoothing only
 };
 
 // Token of virtual key j (the concatenated ranges), or -1 past the keys.
@@ -222,8 +237,9 @@ __device__ __forceinline__ void attn_decode8_f32(uint32_t w, float s, float (&o)
 
 // Writes one fetched tile into LDS (K rows, Vᵀ rows, per-key factors).
 template <bool BF16, bool SMOOTH>
-__device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, const int32_t *lds_starts,
-                                           ChunkCache &cc, const AttnArgs &a) {
+__device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile<SMOOTH> &L, const AttnTile<SMOOTH> *prev,
+                                           const int32_t *lds_starts, ChunkCache &cc, const AttnArgs &a,
+                                           int h) {
   const int t = threadIdx.x;
   const int kk = t & 63, c = t >> 6, kp = t & 31, db = t >> 5;
   uint8_t *krow = L.k + kk * kKRow + 64 * c;
@@ -267,8 +283,9 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, c
   }
   if (t < kAK) {
     float gk = 0.0f, gv = 0.0f;
+    int32_t kci = -1;                      // K-smoothing: the key's append (−1 past the keys)
     if (f.tok >= 0) {
-      if constexpr (!BF16) {
+      if constexpr (SMOOTH) {
         if (f.tok < cc.lo || f.tok >= cc.hi) {
           const int64_t ci = lds_starts != nullptr ? attn_chunk_of(lds_starts, a.n_chunks, (int64_t)f.tok)
                                                    : attn_chunk_of(a.chunk_start, a.n_chunks, (int64_t)f.tok);
@@ -280,6 +297,18 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, c
         }
         gk = cc.gk;
         gv = cc.gv;
+        kci = cc.ci;
+      } else if constexpr (!BF16) {
+        if (f.tok < cc.lo || f.tok >= cc.hi) {
+          const int64_t ci = lds_starts != nullptr ? attn_chunk_of(lds_starts, a.n_chunks, (int64_t)f.tok)
+                                                   : attn_chunk_of(a.chunk_start, a.n_chunks, (int64_t)f.tok);
+          cc.lo = lds_starts != nullptr ? lds_starts[ci] : (int32_t)a.chunk_start[ci];
+          cc.hi = lds_starts != nullptr ? lds_starts[ci + 1] : (int32_t)a.chunk_start[ci + 1];
+          cc.gk = a.gscale[2 * ci] * a.qk_scale;
+          cc.gv = a.gscale[2 * ci + 1];
+        }
+        gk = cc.gk;
+        gv = cc.gv;
       } else {
         gk = a.qk_scale;
         gv = 1.0f;
@@ -287,15 +316,7 @@ __device__ __forceinline__ void tile_store(const TileIn<BF16> &f, AttnTile &L, c
     }
     L.gk[t] = gk;
     L.gv[t] = gv;
-    if constexpr (SMOOTH) {
-      // wave 0 (keys 0..63): the append of each key, and whether one append
-      // holds every key of the tile (key 0 always exists)
-      const int32_t ck = f.tok >= 0 ? cc.ci : -1;
-      L.ck[t] = ck;
-      const int32_t ck0 = __shfl(ck, 0, 64);
-      const uint64_t others = __ballot(f.tok >= 0 && ck != ck0);     // the whole wave votes
-      if (t == 0) L.uni = others == 0 ? ck0 : -1;
-    }
+    if constexpr (SMOOTH) L.ck[t] = kci;
   }
 }
 
@@ -328,10 +349,39 @@ __device__ __forceinline__ float attn_center_dot(const AttnArgs &a, int64_t q, i
   return acc * a.qk_scale;
 }
 
+// The same q·μ from the query's fp16 fragments, the centre row read from
+// memory with all its loads in flight at once (fp16 holds the bf16 centre
+// exactly for |μ| in [2^-14, 65504]; smaller centres lose low bits, a change
+// far below the scores' rounding).  Used where the score registers are free.
+__device__ __forceinline__ float attn_center_dot_q(const AttnArgs &a, const f16x8 (&qf)[8], int h, int hh,
+                                                   int32_t c) {
+  const uint16_t *mr = a.kcenter + ((int64_t)c * a.heads + h) * kAD + 8 * hh;
+  u32x4 raw[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) raw[st] = *reinterpret_cast<const u32x4 *>(mr + 16 * st);
+  float acc = 0.0f;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    f16x8 m;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      m[2 * e] = (_Float16)bf16_bits_to_f32(raw[st][e] & 0xFFFFu);
+      m[2 * e + 1] = (_Float16)bf16_bits_to_f32(raw[st][e] >> 16);
+    }
+    const f16x8 q = qf[st];
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(q, q, 0, 1), __builtin_shufflevector(m, m, 0, 1), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(q, q, 2, 3), __builtin_shufflevector(m, m, 2, 3), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(q, q, 4, 5), __builtin_shufflevector(m, m, 4, 5), acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(q, q, 6, 7), __builtin_shufflevector(m, m, 6, 7), acc, false);
+  }
+  acc += __shfl_xor(acc, 32, 64);
+  return acc * a.qk_scale;
+}
+
 template <bool BF16, bool SMOOTH>
 __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
   static_assert(!(BF16 && SMOOTH), "K-smoothing applies to the NVFP4 cache only");
-  __shared__ __attribute__((aligned(16))) AttnLds L;
+  __shared__ __attribute__((aligned(16))) AttnLds<SMOOTH> L;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 31, hh = lane >> 5;
   const int h = blockIdx.y, split = blockIdx.z;
@@ -342,7 +392,7 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
 
   bool starts_in_lds = false;
   if constexpr (!BF16) {
-    starts_in_lds = a.n_chunks < kAttnLdsStarts;
+    starts_in_lds = a.n_chunks < attn_lds_starts<SMOOTH>();
     if (starts_in_lds)
       for (int64_t i = threadIdx.x; i <= a.n_chunks; i += kAThreads) L.starts[i] = (int32_t)a.chunk_start[i];
   }
@@ -371,7 +421,11 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
   }
 
   float m = -__builtin_huge_valf(), l = 0.0f;
-  int32_t cb = -1;          // K-smoothing: the append whose q·μ is in L.bq
+  // K-smoothing: q·μ of the previous tile's last append (cbp) is in slot
+  // L.bq[sp]; a tile ending in another append writes that one's into the other
+  // slot, which becomes the current one after the tile
+  int32_t cbp = -1;
+  int sp = 0;
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -385,30 +439,41 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
   if constexpr (!BF16) {
     if (starts_in_lds) __syncthreads();
   }
-  tile_store<BF16, SMOOTH>(fin, L.buf[0], lds_starts, cc, a);
+  tile_store<BF16, SMOOTH>(fin, L.buf[0], nullptr, lds_starts, cc, a, h);
   __syncthreads();
   if (j0 + kAK < j1) tile_fetch<BF16>(fin, a, h, j0 + kAK, j1);
   int cur = 0;
   for (int64_t jt = j0; jt < j1; jt += kAK, cur ^= 1) {
+    // K-smoothing: this tile's append indices, one key per lane, read before
+    // the next tile's decode hides the read's latency
+    int32_t ckl = -1;
+    if constexpr (SMOOTH) ckl = L.buf[cur].ck[lane];
     // decode the next tile into the other buffer (its loads were issued one
     // tile ago), then fetch the one after it
     if (jt + kAK < j1) {
-      tile_store<BF16, SMOOTH>(fin, L.buf[cur ^ 1], lds_starts, cc, a);
+      tile_store<BF16, SMOOTH>(fin, L.buf[cur ^ 1], &L.buf[cur], lds_starts, cc, a, h);
       if (jt + 2 * kAK < j1) tile_fetch<BF16>(fin, a, h, jt + 2 * kAK, j1);
     }
-    const AttnTile &B = L.buf[cur];
+    const AttnTile<SMOOTH> &B = L.buf[cur];
 
     // Keys of a smoothed cache are E2M1·S·g + μ: each score gains q·μ of its
-    // key's append.  A tile inside one append (the usual case) needs one
-    // value per query, found here before the score registers are in use and
-    // kept for the next tiles; a tile over several appends adds the value of
-    // each run of keys after the products (below).
+    // key's append.  Every wave reads the tile's append indices (one key per
+    // lane) and finds whether one append holds the tile and which append its
+    // last key is in; q·μ of that last append is computed here, before the
+    // score registers are in use, unless the previous tile ended in the same
+    // append, and a tile that starts in the previous tile's append finds that
+    // value in the other slot.  Any other append (a tile over three or more,
+    // or the first tile of a split that starts in another append) is read
+    // from memory where it is needed.
+    int32_t cl = -1, scl = 0;
+    bool one_append = false;
     if constexpr (SMOOTH) {
-      const int32_t uni = __builtin_amdgcn_readfirstlane(B.uni);
-      if (uni >= 0 && uni != cb) {
-        L.bq[threadIdx.x] = attn_center_dot(a, qc, h, hh, uni);
-        cb = uni;
-      }
+      const uint64_t valid = __ballot(ckl >= 0);                  // a prefix of the keys
+      const int32_t ck0 = __builtin_amdgcn_readfirstlane(ckl);
+      cl = __builtin_amdgcn_readlane(ckl, 63 - __builtin_clzll(valid));
+      one_append = __ballot(ckl >= 0 && ckl != ck0) == 0;
+      scl = cl != cbp ? 1 - sp : sp;
+      if (cl != cbp) L.bq[scl][threadIdx.x] = attn_center_dot_q(a, qf, h, hh, cl);
     }
     // Sᵀ = K·Qᵀ: lane (query r, hh) gets keys 32kb + 8(v/4) + 4hh + v%4
     f32x16 s[2];
@@ -435,9 +500,9 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
     const int kvalid = (j1 - jt) < kAK ? (int)(j1 - jt) : kAK;
     float mt = -__builtin_huge_valf();
     if constexpr (SMOOTH) {
-      if (B.uni >= 0) {
+      if (one_append) {
         // one append holds the tile: the term q·μ of the scaled score
-        const float bq = L.bq[threadIdx.x];
+        const float bq = L.bq[scl][threadIdx.x];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -453,7 +518,6 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
             }
           }
       } else {
-        const int32_t ckl = B.ck[lane];
         uint64_t runs = __ballot(lane == 0 || ckl != B.ck[lane == 0 ? 0 : lane - 1]);
         while (runs != 0) {
           const int k0 = __builtin_ctzll(runs);
@@ -461,11 +525,9 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
           const int k1 = runs != 0 ? __builtin_ctzll(runs) : kAK;
           const int32_t c = __builtin_amdgcn_readfirstlane(B.ck[k0]);
           if (c < 0) continue;                       // keys past the end (masked below)
-          if (c != cb) {
-            L.bq[threadIdx.x] = attn_center_dot(a, qc, h, hh, c);
-            cb = c;
-          }
-          const float bi = L.bq[threadIdx.x] / B.gk[k0];   // enters before the key factor
+          const float b = c == cl ? L.bq[scl][threadIdx.x]
+                                  : (c == cbp ? L.bq[sp][threadIdx.x] : attn_center_dot(a, qc, h, hh, c));
+          const float bi = b / B.gk[k0];             // enters before the key factor
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -565,6 +627,10 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
         const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
         o[dbk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[sl], o[dbk], 0, 0, 0);
       }
+    }
+    if constexpr (SMOOTH) {
+      cbp = cl;
+      sp = scl;
     }
     // every wave has read tile `cur` and stored the next one
     __syncthreads();

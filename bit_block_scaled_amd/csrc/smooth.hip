@@ -14,13 +14,16 @@
 // initialisation: every partial sum is written before it is read.
 //
 // Three launches, each a plain HBM stream:
-//   k_kv_colsum  — workgroups own 128 tokens x 512 channels; every lane sums 8
-//                  channels over 32 tokens (16-byte loads along the channels),
-//                  the four token rows of a workgroup meet in LDS, and the
-//                  workgroup stores its 128-token partial sum of each channel;
-//   k_kv_center  — one thread per channel adds the partial sums of all token
-//                  strips, turns the sum into μ and writes it to the cache's
-//                  centre row of this append;
+//   k_kv_colsum  — workgroups own a strip of tokens (sized so that about 512
+//                  workgroups cover the chunk) x 512 channels; every lane sums
+//                  8 channels over every fourth token of the strip (16-byte
+//                  loads along the channels, four in flight), the four token
+//                  rows of a workgroup meet in LDS, and the workgroup stores
+//                  its partial sum of each channel;
+//   k_kv_center  — 64 channels per workgroup: its four waves add every
+//                  fourth strip's partial sums, meet in LDS, and one thread
+//                  per channel turns the sum into μ and writes it to the
+//                  cache's centre row of this append;
 //   k_kv_smooth_apply — K' into the workspace, 8 channels per lane.
 // The quantiser then encodes K' (and V) as for an unsmoothed append.
 #include "device_common.h"
@@ -31,8 +34,17 @@ namespace nvfp4 {
 constexpr int kSmThreads = 256;
 constexpr int kSmChan = 512;              // channels per colsum workgroup (64 lanes x 8)
 constexpr int kSmRows = kSmThreads / 64;  // token rows per colsum workgroup
-constexpr int kSmPerRow = 32;             // tokens per row
-constexpr int kSmStrip = kSmRows * kSmPerRow;
+constexpr int kSmUnroll = 4;              // loads of a lane in flight together
+constexpr int kSmTargetWgs = 512;         // colsum workgroups aimed at (two per CU)
+
+// Tokens per colsum strip: a multiple of 16 (4 rows x 4 loads in flight),
+// long enough that about kSmTargetWgs workgroups cover the chunk.
+static int64_t smooth_strip(int64_t T, int64_t e) {
+  const int64_t cgroups = (e + kSmChan - 1) / kSmChan;
+  int64_t strip = (T * cgroups + kSmTargetWgs - 1) / kSmTargetWgs;
+  strip = (strip + kSmRows * kSmUnroll - 1) / (kSmRows * kSmUnroll) * (kSmRows * kSmUnroll);
+  return strip < kSmRows * kSmUnroll ? kSmRows * kSmUnroll : strip;
+}
 
 // The key's count of 2^-24 steps, nearest-even, saturated at ±2^38 (exact in
 // binary64: a bf16 times 2^24 needs 8 significant bits).
@@ -43,22 +55,28 @@ __device__ __forceinline__ int64_t grid_steps(uint32_t bf16) {
   return (int64_t)d;
 }
 
-__global__ void __launch_bounds__(kSmThreads) k_kv_colsum(SmoothArgs a) {
+__global__ void __launch_bounds__(kSmThreads) k_kv_colsum(SmoothArgs a, int64_t strip) {
   __shared__ int64_t red[kSmRows][64][8];
   const int lane = threadIdx.x & 63, row = threadIdx.x >> 6;
   const int64_t c0 = (int64_t)blockIdx.y * kSmChan + 8 * lane;
-  const int64_t t0 = (int64_t)blockIdx.x * kSmStrip + row;
+  const int64_t t0 = (int64_t)blockIdx.x * strip + row;
+  int64_t t1 = t0 - row + strip;
+  t1 = t1 < a.T ? t1 : a.T;
   int64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c0 < a.e) {
-#pragma unroll 4
-    for (int i = 0; i < kSmPerRow; ++i) {
-      const int64_t t = t0 + (int64_t)kSmRows * i;
-      if (t < a.T) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.k + t * a.ld + c0);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    for (int64_t tb = t0; tb < t1; tb += kSmRows * kSmUnroll) {
+      u32x4 v[kSmUnroll];
+#pragma unroll
+      for (int i = 0; i < kSmUnroll; ++i) {
+        const int64_t t = tb + (int64_t)kSmRows * i;
+        v[i] = t < t1 ? *reinterpret_cast<const u32x4 *>(a.k + t * a.ld + c0) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < kSmUnroll; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          acc[2 * k] += grid_steps(w[k] & 0xFFFFu);
+          acc[2 * k] += grid_steps(w[k] & 0xFFFFu);          // +0 steps for the padding zeros
           acc[2 * k + 1] += grid_steps(w[k] >> 16);
         }
       }
@@ -100,12 +118,28 @@ __device__ __forceinline__ uint16_t bf16_rne_from_f64(double v) {
   return (uint16_t)(sign | (exp << 7) | (uint32_t)keep);
 }
 
-__global__ void __launch_bounds__(kSmThreads) k_kv_center(SmoothArgs a) {
-  const int64_t c = (int64_t)blockIdx.x * kSmThreads + threadIdx.x;
-  if (c >= a.e) return;
-  const int64_t strips = (a.T + kSmStrip - 1) / kSmStrip;
+// Workgroups own 64 channels; the four waves add every fourth strip's
+// partial sums and meet in LDS.
+__global__ void __launch_bounds__(kSmThreads) k_kv_center(SmoothArgs a, int64_t strips) {
+  __shared__ int64_t red[kSmRows][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t c = (int64_t)blockIdx.x * 64 + lane;
   int64_t S = 0;                                   // exact: |S| <= 2^62
-  for (int64_t p = 0; p < strips; ++p) S += a.partials[p * a.e + c];
+  if (c < a.e) {
+    int64_t p = w;
+    for (; p + kSmRows * (kSmUnroll - 1) < strips; p += kSmRows * kSmUnroll) {
+      int64_t v[kSmUnroll];
+#pragma unroll
+      for (int i = 0; i < kSmUnroll; ++i) v[i] = a.partials[(p + kSmRows * i) * a.e + c];
+#pragma unroll
+      for (int i = 0; i < kSmUnroll; ++i) S += v[i];
+    }
+    for (; p < strips; p += kSmRows) S += a.partials[p * a.e + c];
+  }
+  red[w][lane] = S;
+  __syncthreads();
+  if (w != 0 || c >= a.e) return;
+  S = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
   const double mean = (double)S / (double)a.T;
   a.center[c] = bf16_rne_from_f64(mean * 0x1p-24);
 }
@@ -128,19 +162,23 @@ __global__ void __launch_bounds__(kSmThreads) k_kv_smooth_apply(SmoothArgs a) {
   *reinterpret_cast<u32x4 *>(a.out + t * a.e + c) = u32x4{o[0], o[1], o[2], o[3]};
 }
 
-int64_t smooth_partial_count(int64_t T, int64_t e) { return (T + kSmStrip - 1) / kSmStrip * e; }
+int64_t smooth_partial_count(int64_t T, int64_t e) {
+  const int64_t strip = smooth_strip(T, e);
+  return (T + strip - 1) / strip * e;
+}
 
 hipError_t launch_kv_smooth(const SmoothArgs &a, hipStream_t stream) {
   if (a.T < 1 || a.e < 8 || a.e % 8) return hipErrorInvalidValue;
-  const int64_t strips = (a.T + kSmStrip - 1) / kSmStrip, cgroups = (a.e + kSmChan - 1) / kSmChan;
+  const int64_t strip = smooth_strip(a.T, a.e);
+  const int64_t strips = (a.T + strip - 1) / strip, cgroups = (a.e + kSmChan - 1) / kSmChan;
   const int64_t groups = a.T * (a.e / 8);
   const int64_t apply_blocks = (groups + kSmThreads - 1) / kSmThreads;
   if (strips > 0x7FFFFFFF || cgroups > 65535 || apply_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_kv_colsum, dim3((unsigned)strips, (unsigned)cgroups), dim3(kSmThreads), 0, stream, a);
+  hipLaunchKernelGGL(k_kv_colsum, dim3((unsigned)strips, (unsigned)cgroups), dim3(kSmThreads), 0, stream, a,
+                     strip);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_kv_center, dim3((unsigned)((a.e + kSmThreads - 1) / kSmThreads)), dim3(kSmThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL(k_kv_center, dim3((unsigned)((a.e + 63) / 64)), dim3(kSmThreads), 0, stream, a, strips);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_kv_smooth_apply, dim3((unsigned)apply_blocks), dim3(kSmThreads), 0, stream, a);
   return hipGetLastError();
