@@ -32,7 +32,7 @@ device copy) with p10/p50/p90 over repetitions; the HBM-bound ones after a
 
 Other modes: --copy-only (1 GiB copy, for rocprofv3 counter calibration),
 --gemm-clock (QKV GEMM on benchmark vs constant operands), --wgrad-only (the
-weight-gradient configuration alone).
+weight-gradient configuration alone), --kv-smooth-only (the K-smoothed cache alone).
 """
 
 from __future__ import annotations
@@ -87,6 +87,9 @@ def parse():
     ap.add_argument("--wgrad-only", action="store_true",
                     help="run only the FFN weight-gradient configuration (Hadamard-transformed operands and "
                          "their GEMM) and print its timings (for rocprofv3)")
+    ap.add_argument("--kv-smooth-only", action="store_true",
+                    help="run only the K-smoothed KV legs (8-frame adaptive appends, 880-token appends, "
+                         "attention over the smoothed cache) and print their timings (for rocprofv3)")
     ap.add_argument("--gemm-clock", action="store_true",
                     help="run only the QKV GEMM, 20 launches on the benchmark's operands, then 20 on "
                          "constant-byte operands (for rocprofv3 --pmc GRBM_GUI_ACTIVE)")
@@ -240,6 +243,11 @@ def main():
     if a.wgrad_only:
         kernels = {}
         wgrad_leg(kernels, nv, torch, np, workloads, dev, up, CacheFlush(torch, dev))
+        print(json.dumps({"kernels": kernels}))
+        return
+    if a.kv_smooth_only:
+        kernels = {}
+        kv_smooth_leg(kernels, nv, torch, np, workloads, dev, up, CacheFlush(torch, dev))
         print(json.dumps({"kernels": kernels}))
         return
 
@@ -619,6 +627,33 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
 
     wgrad_leg(kernels, nv, torch, np, workloads, dev, up, flush)
     return round(float(copy_gbs), 1)
+
+
+def kv_smooth_leg(kernels, nv, torch, np, workloads, dev, up, flush):
+    """The K-smoothed cache alone (a short program for rocprofv3): the
+    65536-token workload in 8-frame chunks with adaptive scales and in
+    880-token appends, then attention of 880 queries over the latter."""
+    Kb, Vb, sizes = workloads.kv()
+    kd, vd = up(Kb), up(Vb)
+    T = Kb.shape[0]
+    del Kb, Vb
+    sizes8 = workloads.kv_chunk_sizes(T, 8 * workloads.KV_CHUNK)
+    for name, sz, adapt in (("8frame_chunks_smoothed_adaptive", sizes8, True), ("sequence_smoothed", sizes, False)):
+        st = np.r_[0, np.cumsum(sz)]
+        cache = nv.KVCache(T, 24, 128, max_chunks=len(sz), device=dev, smooth_k=True)
+
+        def seq(cache=cache, st=st, sz=sz, adapt=adapt):
+            cache.reset()
+            for i in range(len(sz)):
+                cache.append(kd[st[i]:st[i + 1]], vd[st[i]:st[i + 1]], adaptive46=adapt)
+        t = time_us(torch, seq, 3, 1, flush)
+        kernels[f"kv65536_append_{name}_cold"] = {"appends": len(sz), "tokens": T, "us": pct(t)}
+    rng = np.random.default_rng(5)
+    qa = up(workloads.to_bf16_bits(rng.standard_normal((880, 24, 128)).astype(np.float32)))
+    oa = torch.empty_like(qa)
+    ws_a = nv._attention_ws(880, 24, T, dev)
+    t = time_us(torch, lambda: cache.attention(qa, [(0, T)], out=oa, ws=ws_a), 3, 1)
+    kernels["attention_full_nvfp4_smoothed"] = {"queries": 880, "keys": T, "heads": 24, "us": pct(t)}
 
 
 def wgrad_leg(kernels, nv, torch, np, workloads, dev, up, flush):
