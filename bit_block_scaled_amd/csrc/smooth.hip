@@ -14,10 +14,11 @@
 // initialisation: every partial sum is written before it is read.
 //
 // Three launches, each a plain HBM stream:
-//   k_kv_colsum  — workgroups own a strip of tokens (sized so that about 512
+//   k_kv_colsum  — workgroups own a strip of tokens (sized so that about 1024
 //                  workgroups cover the chunk) x 512 channels; every lane sums
 //                  8 channels over every fourth token of the strip (16-byte
-//                  loads along the channels, four in flight), the four token
+//                  loads along the channels, four in flight; grid steps from
+//                  the bf16 bits with integer operations), the four token
 //                  rows of a workgroup meet in LDS, and the workgroup stores
 //                  its partial sum of each channel;
 //   k_kv_center  — 64 channels per workgroup: its four waves add every
@@ -35,7 +36,7 @@ constexpr int kSmThreads = 256;
 constexpr int kSmChan = 512;              // channels per colsum workgroup (64 lanes x 8)
 constexpr int kSmRows = kSmThreads / 64;  // token rows per colsum workgroup
 constexpr int kSmUnroll = 4;              // loads of a lane in flight together
-constexpr int kSmTargetWgs = 512;         // colsum workgroups aimed at (two per CU)
+constexpr int kSmTargetWgs = 1024;        // colsum workgroups aimed at (four per CU)
 
 // Tokens per colsum strip: a multiple of 16 (4 rows x 4 loads in flight),
 // long enough that about kSmTargetWgs workgroups cover the chunk.
@@ -46,13 +47,29 @@ static int64_t smooth_strip(int64_t T, int64_t e) {
   return strip < kSmRows * kSmUnroll ? kSmRows * kSmUnroll : strip;
 }
 
-// The key's count of 2^-24 steps, nearest-even, saturated at ±2^38 (exact in
-// binary64: a bf16 times 2^24 needs 8 significant bits).
-__device__ __forceinline__ int64_t grid_steps(uint32_t bf16) {
-  double d = (double)bf16_bits_to_f32(bf16) * 16777216.0;
-  d = __builtin_rint(d);
-  d = d < -274877906944.0 ? -274877906944.0 : (d > 274877906944.0 ? 274877906944.0 : d);
-  return (int64_t)d;
+// The key's count of 2^-24 steps, nearest-even, saturated at ±2^38, from the
+// bf16 bits with 32-bit integer operations: a normal key is sig·2^(e−134),
+// sig = 128 + mantissa, so it is sig·2^s steps with s = e − 110.  For s >= 0
+// the count is exact (sig·2^30 < 2^38; s >= 31 reaches the saturation); for
+// −8 <= s < 0 it is sig shifted right by −s with the nearest-even rule; a
+// smaller key (s < −8, zero and subnormals included) is below half a step.
+// Inputs are finite.
+__device__ __forceinline__ int64_t grid_steps(uint32_t b) {
+  const int s = (int)((b >> 7) & 0xFFu) - 110;
+  const uint32_t sig = 128u + (b & 0x7Fu);
+  int64_t mag;
+  if (s >= 31) {
+    mag = int64_t(1) << 38;
+  } else if (s >= 0) {
+    mag = (int64_t)((uint64_t)sig << s);
+  } else if (s >= -8) {
+    const int r = -s;
+    const uint32_t q = sig >> r, rem = sig & ((1u << r) - 1u), half = 1u << (r - 1);
+    mag = (int64_t)(q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u));
+  } else {
+    mag = 0;
+  }
+  return (b & 0x8000u) ? -mag : mag;
 }
 
 __global__ void __launch_bounds__(kSmThreads) k_kv_colsum(SmoothArgs a, int64_t strip) {
