@@ -17,8 +17,8 @@
 //   k_kv_colsum  — workgroups own a strip of tokens (sized so that about 1024
 //                  workgroups cover the chunk) x 512 channels; every lane sums
 //                  8 channels over every fourth token of the strip (16-byte
-//                  loads along the channels, four in flight; grid steps from
-//                  the bf16 bits with integer operations), the four token
+//                  loads along the channels, four in flight; grid steps in
+//                  binary32, lane sums in exact binary64), the four token
 //                  rows of a workgroup meet in LDS, and the workgroup stores
 //                  its partial sum of each channel;
 //   k_kv_center  — 64 channels per workgroup: its four waves add every
@@ -44,32 +44,20 @@ static int64_t smooth_strip(int64_t T, int64_t e) {
   const int64_t cgroups = (e + kSmChan - 1) / kSmChan;
   int64_t strip = (T * cgroups + kSmTargetWgs - 1) / kSmTargetWgs;
   strip = (strip + kSmRows * kSmUnroll - 1) / (kSmRows * kSmUnroll) * (kSmRows * kSmUnroll);
+  strip = strip > (int64_t(1) << 17) ? (int64_t(1) << 17) : strip;   // exact binary64 lane sums
   return strip < kSmRows * kSmUnroll ? kSmRows * kSmUnroll : strip;
 }
 
-// The key's count of 2^-24 steps, nearest-even, saturated at ±2^38, from the
-// bf16 bits with 32-bit integer operations: a normal key is sig·2^(e−134),
-// sig = 128 + mantissa, so it is sig·2^s steps with s = e − 110.  For s >= 0
-// the count is exact (sig·2^30 < 2^38; s >= 31 reaches the saturation); for
-// −8 <= s < 0 it is sig shifted right by −s with the nearest-even rule; a
-// smaller key (s < −8, zero and subnormals included) is below half a step.
-// Inputs are finite.
-__device__ __forceinline__ int64_t grid_steps(uint32_t b) {
-  const int s = (int)((b >> 7) & 0xFFu) - 110;
-  const uint32_t sig = 128u + (b & 0x7Fu);
-  int64_t mag;
-  if (s >= 31) {
-    mag = int64_t(1) << 38;
-  } else if (s >= 0) {
-    mag = (int64_t)((uint64_t)sig << s);
-  } else if (s >= -8) {
-    const int r = -s;
-    const uint32_t q = sig >> r, rem = sig & ((1u << r) - 1u), half = 1u << (r - 1);
-    mag = (int64_t)(q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u));
-  } else {
-    mag = 0;
-  }
-  return (b & 0x8000u) ? -mag : mag;
+// The key's count of 2^-24 steps, nearest-even, saturated at ±2^38, in
+// binary32 without branches: K·2^24 is exact (8 significant bits; keys beyond
+// 2^104 become infinite and saturate), round-to-nearest-even to an integer is
+// exact, and so is the saturation at ±2^38.  The lanes add these counts in
+// binary64, exact while a lane adds at most 2^15 of them (strips are capped at
+// 2^17 tokens: 4 rows of 2^15), and convert to 64-bit integers once.
+__device__ __forceinline__ float grid_steps_f32(uint32_t bf16) {
+  float x = __builtin_rintf(bf16_bits_to_f32(bf16) * 16777216.0f);
+  x = __builtin_fmaxf(x, -274877906944.0f);
+  return __builtin_fminf(x, 274877906944.0f);
 }
 
 __global__ void __launch_bounds__(kSmThreads) k_kv_colsum(SmoothArgs a, int64_t strip) {
@@ -79,7 +67,7 @@ __global__ void __launch_bounds__(kSmThreads) k_kv_colsum(SmoothArgs a, int64_t 
   const int64_t t0 = (int64_t)blockIdx.x * strip + row;
   int64_t t1 = t0 - row + strip;
   t1 = t1 < a.T ? t1 : a.T;
-  int64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  double accd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c0 < a.e) {
     for (int64_t tb = t0; tb < t1; tb += kSmRows * kSmUnroll) {
       u32x4 v[kSmUnroll];
@@ -93,14 +81,14 @@ __global__ void __launch_bounds__(kSmThreads) k_kv_colsum(SmoothArgs a, int64_t 
         const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          acc[2 * k] += grid_steps(w[k] & 0xFFFFu);          // +0 steps for the padding zeros
-          acc[2 * k + 1] += grid_steps(w[k] >> 16);
+          accd[2 * k] += (double)grid_steps_f32(w[k] & 0xFFFFu);   // +0 steps for the padding zeros
+          accd[2 * k + 1] += (double)grid_steps_f32(w[k] >> 16);
         }
       }
     }
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) red[row][lane][k] = acc[k];
+  for (int k = 0; k < 8; ++k) red[row][lane][k] = (int64_t)accd[k];
   __syncthreads();
   // thread j adds channels 2j and 2j + 1 of the workgroup's 512 and stores
   // the strip's partial sums
