@@ -417,12 +417,12 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
   // load nothing, and their slots are never read
   if constexpr (STREAM) {
     const QuantTensor &T = args.t[0];
-    const int wave_base = threadIdx.x & ~63;
+    [[maybe_unused]] const int wave_base = threadIdx.x & ~63;          // device pass only
 #pragma unroll
     for (int i = 0; i < ULDS; ++i) {
       const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + threadIdx.x;
       if (UMAX + i < u && b < 2 * T.units) {
-        const u32x4 *p = block_src(T, b);
+        [[maybe_unused]] const u32x4 *p = block_src(T, b);
 #if defined(__HIP_DEVICE_COMPILE__)      // device-only builtin; the host pass only parses the kernel
         __builtin_amdgcn_global_load_lds(p, &lds_blk[(2 * i) * kResThreads + wave_base], 16, 0, 0);
         __builtin_amdgcn_global_load_lds(p + 1, &lds_blk[(2 * i + 1) * kResThreads + wave_base], 16, 0, 0);
