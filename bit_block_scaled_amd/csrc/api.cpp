@@ -349,15 +349,14 @@ int nvfp4_kv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t
 }
 
 // Scratch a K-smoothed cache needs after an append's own workspace: the
-// per-strip channel sums, then the smoothed keys [T, e] (no initialisation).
+// per-strip channel sums (no initialisation).
 struct SmoothWs {
-  size_t sums, keys, total;
+  size_t sums, total;
 };
 static SmoothWs smooth_ws(size_t base, int64_t T, int64_t e) {
   SmoothWs w;
   w.sums = round_up(base, 256);
-  w.keys = round_up(w.sums + size_t(nvfp4::smooth_partial_count(T, e)) * sizeof(int64_t), 256);
-  w.total = round_up(w.keys + size_t(T) * size_t(e) * sizeof(uint16_t), 256);
+  w.total = round_up(w.sums + size_t(nvfp4::smooth_partial_count(T, e)) * sizeof(int64_t), 256);
   return w;
 }
 
@@ -370,16 +369,16 @@ int nvfp4_kv_smooth_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t
   return NVFP4_OK;
 }
 
-// Enqueues the K-smoothing of T keys (token stride ld) of the append about to
-// be made as chunk c->n_chunks; returns the smoothed keys ([T, e], dense).
+// Enqueues the channel centres of T keys (token stride ld) of the append
+// about to be made as chunk c->n_chunks; returns that chunk's centre row,
+// which the append's quantiser subtracts as it loads the keys.
 static int enqueue_smoothing(const nvfp4_kv_cache *c, const uint16_t *K, int64_t T, int64_t ld,
                              uint8_t *ws, size_t base, hipStream_t st, const char *who,
-                             const uint16_t **smoothed) {
+                             const uint16_t **center) {
   const int64_t e = c->heads * c->head_dim;
   const SmoothWs w = smooth_ws(base, T, e);
-  nvfp4::SmoothArgs sa{K, T, e, ld, reinterpret_cast<int64_t *>(ws + w.sums), c->k_center + c->n_chunks * e,
-                       reinterpret_cast<uint16_t *>(ws + w.keys)};
-  *smoothed = sa.out;
+  nvfp4::SmoothArgs sa{K, T, e, ld, reinterpret_cast<int64_t *>(ws + w.sums), c->k_center + c->n_chunks * e};
+  *center = sa.center;
   return launched(nvfp4::launch_kv_smooth(sa, st), st, who);
 }
 
@@ -411,14 +410,12 @@ int nvfp4_kv_append_ex(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, 
   const int64_t off = c->n_tokens * e;
   uint8_t *parts = static_cast<uint8_t *>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const uint16_t *kin = K;
-  int64_t kld = ld;
-  if (c->k_center != nullptr) {
-    if ((s = enqueue_smoothing(c, K, T, ld, parts, 2 * kQuantWs, st, "kv_append/smooth", &kin))) return s;
-    kld = e;
-  }
+  const uint16_t *center = nullptr;
+  if (c->k_center != nullptr &&
+      (s = enqueue_smoothing(c, K, T, ld, parts, 2 * kQuantWs, st, "kv_append/smooth", &center)))
+    return s;
   nvfp4::QuantJob jobs[2] = {
-      {kin, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T, e, kld},
+      {K, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, parts, T, e, ld, center},
       {V, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
        parts + kQuantWs, T, e, ld}};
   nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
@@ -502,14 +499,13 @@ int nvfp4_qkv_append(nvfp4_kv_cache *c, const uint16_t *x, int64_t T, int64_t D,
   }
   if ((s = launched(nvfp4::launch_gemm(a, st), st, "qkv_append/gemm"))) return s;
   const int64_t off = c->n_tokens * hd;
-  const uint16_t *kin = QKV + hd;
-  int64_t kld = N;
-  if (c->k_center != nullptr) {
-    if ((s = enqueue_smoothing(c, QKV + hd, T, N, base, w.total, st, "qkv_append/smooth", &kin))) return s;
-    kld = hd;
-  }
+  const uint16_t *center = nullptr;
+  if (c->k_center != nullptr &&
+      (s = enqueue_smoothing(c, QKV + hd, T, N, base, w.total, st, "qkv_append/smooth", &center)))
+    return s;
   nvfp4::QuantJob jobs[2] = {
-      {kin, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, base + w.app, T, hd, kld},
+      {QKV + hd, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, base + w.app, T, hd, N,
+       center},
       {QKV + 2 * hd, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
        base + w.app + kQuantWs, T, hd, N}};
   const nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};

@@ -33,6 +33,10 @@ struct QuantJob {
   float *gscale;
   void *scratch;
   int64_t rows, cols, ld;
+  // K-smoothing: bf16 [cols] channel centres subtracted from every row as it
+  // is loaded, bf16_rne(fl32(x − center)); null for none.  Used by the KV
+  // append (two tensors per launch).
+  const uint16_t *center = nullptr;
 };
 
 // KV-cache bookkeeping written by the encode launch of an append:
@@ -118,14 +122,14 @@ hipError_t launch_kv_dequant(const KvDequantArgs &a, hipStream_t stream);
 
 // K-smoothing of one appended chunk: keys k [T, e] bf16 (token t at k + t·ld,
 // e and ld multiples of 8, 16-byte aligned), the channel centres written to
-// center [e] (bf16), the smoothed keys to out [T, e] (dense).  partials holds
-// smooth_partial_count(T, e) 64-bit integers, written before they are read.
+// center [e] (bf16; the quantiser subtracts them as it loads K, see
+// QuantJob::center).  partials holds smooth_partial_count(T, e) 64-bit
+// integers, written before they are read.
 struct SmoothArgs {
   const uint16_t *k;
   int64_t T, e, ld;
   int64_t *partials;
   uint16_t *center;
-  uint16_t *out;
 };
 int64_t smooth_partial_count(int64_t T, int64_t e);
 hipError_t launch_kv_smooth(const SmoothArgs &a, hipStream_t stream);

@@ -49,6 +49,7 @@ struct QuantTensor {
   int64_t units;         // elements / 32
   uint32_t units_per_row;
   int64_t ld;            // input elements between row starts
+  const uint16_t *center;  // K-smoothing: bf16 per column, subtracted on load (or null)
 };
 
 // First 16-byte chunk of unit u in the (possibly row-strided) input.
@@ -62,12 +63,30 @@ __device__ __forceinline__ const u32x4 *block_src(const QuantTensor &T, int64_t 
   return unit_src(T, b >> 1) + 2 * (b & 1);
 }
 
-// Block b of the tensor as 8 bf16 pairs (two 16-byte loads).
+// K-smoothing: block b's 16 elements minus the centres of their columns,
+// bf16_rne(fl32(x − μ)) (a no-op without centres).
+__device__ __forceinline__ void center_block(const QuantTensor &T, int64_t b, uint32_t (&w)[8]) {
+  if (T.center == nullptr) return;
+  const uint32_t cb = (uint32_t)b % (2u * T.units_per_row);          // block within its row
+  const u32x4 *m = reinterpret_cast<const u32x4 *>(T.center + 16 * cb);
+  const u32x4 m0 = m[0], m1 = m[1];
+  const uint32_t mu[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    w[k] = pack_bf16x2(bf16_bits_to_f32(w[k] & 0xFFFFu) - bf16_bits_to_f32(mu[k] & 0xFFFFu),
+                       bf16_bits_to_f32(w[k] >> 16) - bf16_bits_to_f32(mu[k] >> 16));
+}
+
+// Block b of the tensor as 8 bf16 pairs (two 16-byte loads), centred when
+// the tensor has centres (CENTER: only the kernels that take K/V pairs carry
+// that code; the single-tensor ones never get centres).
+template <bool CENTER = true>
 __device__ __forceinline__ void load_block(const QuantTensor &T, int64_t b, uint32_t (&w)[8]) {
   const u32x4 *p = block_src(T, b);
   const u32x4 lo = p[0], hi = p[1];
   w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
   w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+  if constexpr (CENTER) center_block(T, b, w);
 }
 
 // Largest magnitude (bf16 pattern) of 8 bf16 pairs.
@@ -296,7 +315,7 @@ __global__ void __launch_bounds__(kThreads) k_encode_2d(QuantArgs args, int npar
   uint32_t am = 0;
   for (int64_t r = r0; r < r1; ++r) {
     uint32_t w[8];
-    load_block(T, r * nbc + bc, w);
+    load_block<false>(T, r * nbc + bc, w);
     const uint32_t a = absmax16(w);
     am = am > a ? am : a;
   }
@@ -307,7 +326,7 @@ __global__ void __launch_bounds__(kThreads) k_encode_2d(QuantArgs args, int npar
   for (int64_t r = r0; r < r1; ++r) {
     uint32_t w[8], lo, hi;
     const int64_t b = r * nbc + bc;
-    load_block(T, b, w);
+    load_block<false>(T, b, w);
     encode_codes(w, rc, lo, hi);
     codes[b] = u32x2{lo, hi};
     scales[b] = (uint8_t)S;
@@ -344,7 +363,7 @@ constexpr int kLdsBlocks = 4;                 // STREAM: resident blocks per thr
 // This thread's part of the |x| maximum of workgroup p's share of a tensor
 // (the blocks that workgroup p loads, including its streamed chunks): read by
 // a workgroup whose wait for p's slot expired.
-template <bool STREAM>
+template <bool STREAM, bool CENTER>
 __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
   const int64_t nb = 2 * T.units;
   uint32_t m = 0;
@@ -352,7 +371,7 @@ __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
     const int64_t b = ((int64_t)p * u + i) * kResThreads + threadIdx.x;
     if (b < nb) {
       uint32_t w[8];
-      load_block(T, b, w);
+      load_block<CENTER>(T, b, w);
       const uint32_t a = absmax16(w);
       m = m > a ? m : a;
     }
@@ -361,7 +380,7 @@ __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
     const int64_t cstride = (int64_t)nwg * kResThreads;
     for (int64_t b = cstride * u + (int64_t)p * kResThreads + threadIdx.x; b < nb; b += cstride) {
       uint32_t w[8];
-      load_block(T, b, w);
+      load_block<CENTER>(T, b, w);
       const uint32_t a = absmax16(w);
       m = m > a ? m : a;
     }
@@ -450,6 +469,17 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
       w[j][i][4] = hi.x; w[j][i][5] = hi.y; w[j][i][6] = hi.z; w[j][i][7] = hi.w;
     }
   }
+  // K-smoothing (K/V pairs only): centre the blocks once all loads are in
+  // flight (blocks past the tensor stay 0: never encoded, maximum unused)
+  if constexpr (NJ == 2) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < UMAX; ++i) {
+        const int64_t b = ((int64_t)k * u + i) * kResThreads + threadIdx.x;
+        if (args.t[j].center != nullptr && i < u && b < 2 * args.t[j].units) center_block(args.t[j], b, w[j][i]);
+      }
+  }
   // streamed blocks (STREAM): b = nwg·u·1024 + (s·nwg + k)·1024 + thread
   uint32_t ms = 0, ml = 0;
   if constexpr (STREAM) {
@@ -462,7 +492,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
       for (int i = 0; i < kStreamU; ++i) {
         const int64_t b = b0 + i * cstride;
         if (b < nb) {
-          load_block(T, b, v[i]);
+          load_block<false>(T, b, v[i]);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[i][e] = 0u;
@@ -566,7 +596,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
       uint32_t md = 0;
       for (int w = 0; w < NW; ++w)
         for (uint64_t mb = miss[j][w]; mb != 0; mb &= mb - 1) {
-          const uint32_t v = share_max<STREAM>(args.t[j], 64 * w + __builtin_ctzll(mb), u, nwg);
+          const uint32_t v = share_max<STREAM, NJ == 2>(args.t[j], 64 * w + __builtin_ctzll(mb), u, nwg);
           md = md > v ? md : v;
         }
       const uint32_t rd = block_max_u32<kResThreads>(md, red2[j]);
@@ -626,7 +656,7 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
         for (int i = 0; i < kStreamU; ++i) {
           const int64_t b = b0 + i * cstride;
           if (b < nb) {
-            load_block(T, b, v[i]);
+            load_block<false>(T, b, v[i]);
           } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[i][e] = 0u;
@@ -716,7 +746,7 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
     // more than the grid's registers hold: keep 8 blocks per thread resident
     // in registers and kLdsBlocks in LDS, and stream the rest (one tensor
     // only; else the two-pass kernels)
-    if (njobs != 1 || !lim.fits_stream[ADAPT]) return false;
+    if (njobs != 1 || !lim.fits_stream[ADAPT] || a.t[0].center != nullptr) return false;   // LDS blocks are not centred
     // the fewest blocks per thread that cover the tensor (every workgroup
     // busy), at most what registers and LDS hold
     const int us = (int)(u < 8 + kLdsBlocks ? u : 8 + kLdsBlocks);
@@ -777,6 +807,7 @@ hipError_t launch_encode_from_partials(const QuantJob &job, const uint32_t *maxi
   a.t[0].units = job.rows * (job.cols / 32);
   a.t[0].units_per_row = (uint32_t)(job.cols / 32);
   a.t[0].ld = job.ld;
+  a.t[0].center = job.center;
   if (nparts < 1 || nparts > 0x7FFFFFFF) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_encode<false>, dim3(encode_blocks(a.t[0].units), 1), dim3(kThreads), 0, stream, a,
                      (int)nparts);
@@ -798,6 +829,7 @@ hipError_t launch_encode2_from_partials(const QuantJob (&jobs)[2], const uint32_
     a.t[i].units = jobs[i].rows * (jobs[i].cols / 32);
     a.t[i].units_per_row = (uint32_t)(jobs[i].cols / 32);
     a.t[i].ld = jobs[i].ld;
+    a.t[i].center = jobs[i].center;
     if (a.t[i].units > max_units) max_units = a.t[i].units;
   }
   if (nparts < 1 || nparts > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -825,8 +857,12 @@ hipError_t launch_quantize(const QuantJob *jobs, int njobs, hipStream_t stream,
     a.t[i].units = jobs[i].rows * (jobs[i].cols / 32);
     a.t[i].units_per_row = (uint32_t)(jobs[i].cols / 32);
     a.t[i].ld = jobs[i].ld;
+    a.t[i].center = jobs[i].center;
     if (a.t[i].units > max_units) max_units = a.t[i].units;
   }
+  // centres are carried by the kernels that take K/V pairs only
+  if (njobs != 2 && a.t[0].center != nullptr) return hipErrorInvalidValue;
+  if (blocks2d && (a.t[0].center != nullptr || (njobs == 2 && a.t[1].center != nullptr))) return hipErrorInvalidValue;
   hipError_t e = hipSuccess;
   if (blocks2d) {             // two passes: tensor amax, then one thread per 16x16 tile
     if (njobs != 1 || adaptive46 || mark != nullptr) return hipErrorInvalidValue;

@@ -8,12 +8,13 @@
 //     z_t = clamp(round_half_even(K[t, c] · 2^24), −2^38, 2^38)
 //     S   = Σ_t z_t                     (exact, 64-bit integers, any order)
 //     μ_c = bf16_rne(fl64(fl64(S) / T) · 2^-24)
-//   smoothed key K'[t, c] = bf16_rne(fl32(K[t, c] − μ_c)).
+//   smoothed key K'[t, c] = bf16_rne(fl32(K[t, c] − μ_c)), formed by the
+//   quantiser as it loads each block of K (the append passes it the centres).
 // Because the sum is exact integer arithmetic, the centre does not depend on
 // the order in which the parts are added.  The workspace needs no
 // initialisation: every partial sum is written before it is read.
 //
-// Three launches, each a plain HBM stream:
+// Two launches before the append's quantiser:
 //   k_kv_colsum  — workgroups own a strip of tokens (sized so that about 1024
 //                  workgroups cover the chunk) x 512 channels; every lane sums
 //                  8 channels over every fourth token of the strip (16-byte
@@ -24,9 +25,9 @@
 //   k_kv_center  — 64 channels per workgroup: its four waves add every
 //                  fourth strip's partial sums, meet in LDS, and one thread
 //                  per channel turns the sum into μ and writes it to the
-//                  cache's centre row of this append;
-//   k_kv_smooth_apply — K' into the workspace, 8 channels per lane.
-// The quantiser then encodes K' (and V) as for an unsmoothed append.
+//                  cache's centre row of this append.
+// The quantiser then reads K once more, centres each block as it loads it,
+// and encodes K' (and V) as for an unsmoothed append.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -149,24 +150,6 @@ __global__ void __launch_bounds__(kSmThreads) k_kv_center(SmoothArgs a, int64_t 
   a.center[c] = bf16_rne_from_f64(mean * 0x1p-24);
 }
 
-__global__ void __launch_bounds__(kSmThreads) k_kv_smooth_apply(SmoothArgs a) {
-  const int64_t per_tok = a.e / 8;
-  const int64_t g = (int64_t)blockIdx.x * kSmThreads + threadIdx.x;
-  if (g >= a.T * per_tok) return;
-  const int64_t t = g / per_tok, c = 8 * (g - t * per_tok);
-  const u32x4 v = *reinterpret_cast<const u32x4 *>(a.k + t * a.ld + c);
-  const u32x4 m = *reinterpret_cast<const u32x4 *>(a.center + c);
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w}, mu[4] = {m.x, m.y, m.z, m.w};
-  uint32_t o[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float lo = bf16_bits_to_f32(w[k] & 0xFFFFu) - bf16_bits_to_f32(mu[k] & 0xFFFFu);
-    const float hi = bf16_bits_to_f32(w[k] >> 16) - bf16_bits_to_f32(mu[k] >> 16);
-    o[k] = pack_bf16x2(lo, hi);
-  }
-  *reinterpret_cast<u32x4 *>(a.out + t * a.e + c) = u32x4{o[0], o[1], o[2], o[3]};
-}
-
 int64_t smooth_partial_count(int64_t T, int64_t e) {
   const int64_t strip = smooth_strip(T, e);
   return (T + strip - 1) / strip * e;
@@ -176,16 +159,12 @@ hipError_t launch_kv_smooth(const SmoothArgs &a, hipStream_t stream) {
   if (a.T < 1 || a.e < 8 || a.e % 8) return hipErrorInvalidValue;
   const int64_t strip = smooth_strip(a.T, a.e);
   const int64_t strips = (a.T + strip - 1) / strip, cgroups = (a.e + kSmChan - 1) / kSmChan;
-  const int64_t groups = a.T * (a.e / 8);
-  const int64_t apply_blocks = (groups + kSmThreads - 1) / kSmThreads;
-  if (strips > 0x7FFFFFFF || cgroups > 65535 || apply_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (strips > 0x7FFFFFFF || cgroups > 65535) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_kv_colsum, dim3((unsigned)strips, (unsigned)cgroups), dim3(kSmThreads), 0, stream, a,
                      strip);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_kv_center, dim3((unsigned)((a.e + 63) / 64)), dim3(kSmThreads), 0, stream, a, strips);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_kv_smooth_apply, dim3((unsigned)apply_blocks), dim3(kSmThreads), 0, stream, a);
   return hipGetLastError();
 }
 

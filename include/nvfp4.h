@@ -272,8 +272,8 @@ int nvfp4_kv_append_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t
 
 /* Extra workspace bytes an append of T tokens to a K-smoothed cache needs,
  * placed after the workspace of nvfp4_kv_append (or nvfp4_qkv_append): the
- * channel sums of each 128-token strip and the smoothed keys.  This part
- * needs no initialisation. */
+ * channel sums of each strip of tokens.  This part needs no
+ * initialisation. */
 int nvfp4_kv_smooth_workspace(int64_t T, int64_t heads, int64_t head_dim, size_t *bytes);
 
 /*

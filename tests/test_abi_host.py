@@ -167,7 +167,7 @@ def test_kv_smoothing_host_checks(L):
     n, m = C.c_size_t(), C.c_size_t()
     assert L.nvfp4_kv_append_workspace(880, 24, 128, C.byref(n)) == 0
     assert L.nvfp4_kv_smooth_workspace(880, 24, 128, C.byref(m)) == 0
-    assert m.value >= 880 * 3072 * 2 + 3072 * 8                    # smoothed keys + channel sums
+    assert 3072 * 8 <= m.value < 880 * 3072                         # channel sums, no copy of the keys
     assert L.nvfp4_kv_smooth_workspace(880, 24, 100, C.byref(m)) == EINVAL
     assert L.nvfp4_kv_smooth_workspace(0, 24, 128, C.byref(m)) == EINVAL
     assert L.nvfp4_kv_smooth_workspace(880, 24, 128, None) == EINVAL
