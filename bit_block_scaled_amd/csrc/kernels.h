@@ -13,12 +13,11 @@ constexpr int kAmaxBlocks = 1024;
 constexpr int kResidentSlots = 1024;
 // Scratch of one quantised tensor, 256-byte aligned, all zero before its first
 // use (the library keeps it valid from one call to the next):
-//   [0, kCtrlOffset)                 resident slots, one (epoch, max) word per workgroup
-//   [kCtrlOffset, kPartialsOffset)   control words: [0] the epoch of the last
-//                                    completed resident call, [1] its arrival counter
+//   [0, kPartialsOffset)             resident slots, one (epoch, max) word per
+//                                    slot; a resident call leaves all of them
+//                                    with its epoch
 //   [kPartialsOffset, kQuantScratchBytes)  partial maxima of the two-pass kernels
-constexpr size_t kCtrlOffset = 8 * size_t(kResidentSlots);
-constexpr size_t kPartialsOffset = kCtrlOffset + 256;
+constexpr size_t kPartialsOffset = 8 * size_t(kResidentSlots);
 constexpr size_t kQuantScratchBytes = kPartialsOffset + 4 * size_t(kAmaxBlocks);
 static_assert(kQuantScratchBytes % 256 == 0, "scratch regions stay 256-byte aligned");
 

@@ -44,7 +44,7 @@ struct QuantTensor {
   uint8_t *codes;        // 16 bytes per 32-element unit
   uint16_t *scales;      // 2 scale bytes per unit
   float *gscale;         // where g is written
-  uint64_t *slots;       // resident launch: kResidentSlots slots, then the control words
+  uint64_t *slots;       // resident launch: kResidentSlots (epoch, max) slots
   uint32_t *partials;    // two-pass launch: kAmaxBlocks partial maxima
   int64_t units;         // elements / 32
   uint32_t units_per_row;
@@ -397,15 +397,17 @@ __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
 // workgroup reads the shares of the workgroups whose slots it has not seen
 // itself, which yields the same A, so the result never depends on scheduling.
 //
-// The epoch that tags the slots of a call is one more than the control word
-// the previous call on the workspace left (0 in a zeroed workspace).  After
-// its poll every workgroup adds one to the arrival counter beside that word;
-// the workgroup that completes the count resets the counter and advances the
-// word.  Every workgroup reads the word before it arrives, so all workgroups of
-// a call use the same epoch even when they do not run at the same time, and a
-// slot is never tagged with an epoch later than the word: a slot left by an
-// earlier call is never taken for a current one.  Because the word lives in
-// device memory, each replay of a captured graph gets a new epoch.
+// The epoch that tags the slots of a call: every call leaves all
+// kResidentSlots slots of each of its tensors with one tag (workgroup k
+// publishes slot k and stamps slots k + i·nwg, i >= 1, with its epoch), so
+// workgroup k takes one more than the largest tag in its own slot of each
+// tensor.  Only workgroup k writes slot k during a call, so every workgroup of
+// a call derives the same epoch, whenever it runs, and that epoch is above
+// every tag a slot of the call's tensors holds: a slot left by an earlier call
+// is never taken for a current one, whatever the grid sizes of the calls and
+// whichever tensors they paired.  Nothing is shared but the slots, so no
+// arrival count is needed.  Because the tags live in device memory, each
+// replay of a captured graph gets a new epoch.
 // STREAM (one tensor, UMAX = 8, u = 8 + kLdsBlocks): the tensor is larger
 // than the registers of the grid hold.  Its first nwg·1024·u blocks stay
 // resident, blocks 0..7 of a thread in registers as above and blocks
@@ -418,9 +420,15 @@ __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
 template <int NJ, int UMAX, bool ADAPT, bool STREAM = false>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
                                                                 int u, uint64_t wait_ticks) {
-  // the call's epoch (control words: [0] last completed epoch, [1] arrivals)
-  uint64_t *ctrl = args.t[0].slots + kResidentSlots;
-  uint64_t epoch = (load_slot(ctrl) + 1) & kEpochMask;
+  const int k = blockIdx.x, nwg = gridDim.x;
+  // the call's epoch: one more than the largest tag of this workgroup's slots
+  uint64_t epoch = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const uint64_t e = load_slot(args.t[j].slots + k) >> 16;
+    epoch = epoch > e ? epoch : e;
+  }
+  epoch = (epoch + 1) & kEpochMask;
   if (epoch == 0) epoch = 1;
   constexpr int NW = kResThreads / 64;
   constexpr int ULDS = STREAM ? kLdsBlocks : 0;
@@ -429,7 +437,6 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
   // LDS-resident blocks, [block][half][thread]: each wave's 16-byte stores and
   // loads cover consecutive addresses
   __shared__ u32x4 lds_blk[STREAM ? 2 * kLdsBlocks * kResThreads : 1];
-  const int k = blockIdx.x, nwg = gridDim.x;
 
   // LDS-resident blocks: loaded straight into LDS (no registers held), lane
   // l of a wave into slot l of the wave's 64-slot run; lanes past the tensor
@@ -529,9 +536,12 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
       m = m > am ? m : am;
     }
     const uint32_t bmax = block_max_u32<kResThreads>(m, red[j]);
-    if (threadIdx.x == 0)
-      __hip_atomic_store(args.t[j].slots + k, (epoch << 16) | bmax, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    // thread 0 publishes slot k; thread i >= 1 stamps slot k + i·nwg (1024
+    // threads cover every slot above the grid)
+    const int64_t s = k + (int64_t)threadIdx.x * nwg;
+    if (s < kResidentSlots)
+      __hip_atomic_store(args.t[j].slots + s, (epoch << 16) | (threadIdx.x == 0 ? bmax : 0u),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // poll: thread p < nwg watches slot p of every tensor
@@ -556,17 +566,6 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
     if (__syncthreads_and(pending == 0)) break;
     if (__syncthreads_or(__builtin_amdgcn_s_memrealtime() > deadline)) break;
     __builtin_amdgcn_s_sleep(1);
-  }
-  // Arrival: every thread of this workgroup read the control word before the
-  // barrier that ended the poll, so no workgroup can see it advanced during
-  // this call.
-  if (threadIdx.x == 0) {
-    const uint64_t before = __hip_atomic_fetch_add(ctrl + 1, uint64_t(1), __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-    if (before == uint64_t(nwg - 1)) {
-      __hip_atomic_store(ctrl + 1, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctrl, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
   // Fold the slots seen and note the unseen ones, behind one barrier.  Every
   // thread left the poll loop through a barrier, after its last read of red[]

@@ -181,10 +181,10 @@ def test_bounded_wait_fallback_gives_the_same_bytes():
 
 # ----------------------------------------------------------------------------
 # The slot protocol of the single-launch quantiser on one reused workspace.
-# Layout of a quantiser workspace (kernels.h): 64-bit slots from byte 0, the
-# control words (last completed epoch, arrival counter) at byte 8192.
+# Layout of a quantiser workspace (kernels.h): 1024 64-bit (epoch << 16 | max)
+# slots from byte 0; every resident call leaves all of them with its epoch.
 
-SLOTS_BYTES, CTRL_OFFSET = 8192, 8192
+SLOTS_BYTES = 8192
 
 
 def _into(x_dev, ws):
@@ -261,25 +261,24 @@ def test_kv_append_expired_wait_then_normal_wait():
 
 
 def test_stale_slots_of_earlier_calls_are_ignored():
-    # A workspace in a state earlier calls leave behind: the control word at
-    # epoch E, every slot tagged E or below and holding the largest finite
-    # bf16 magnitude.  A call on small data must not take any of them.
+    # A workspace in the state an earlier call leaves behind: every slot
+    # tagged with that call's epoch E and holding the largest finite bf16
+    # magnitude.  Calls on small data must not take any of them, and each call
+    # leaves every slot with its own epoch, whatever its grid size.
     M, K = 2048, 3072
     x = workloads.random_matrix(94, M, K, sigma=0.5)
+    tiny = workloads.random_matrix(95, 40, 256, sigma=0.5)
     ws = nv.workspace(nv.quantize_workspace_bytes(M, K))
     E = 0x123456789A
-    slots = np.zeros(SLOTS_BYTES // 8, dtype=np.uint64)
-    slots[0::2] = np.uint64((E << 16) | 0x7F7F)
-    slots[1::2] = np.uint64(((E - 1) << 16) | 0x7F7F)
+    slots = np.full(SLOTS_BYTES // 8, np.uint64((E << 16) | 0x7F7F), dtype=np.uint64)
     ws[:SLOTS_BYTES].copy_(torch.from_numpy(slots.view(np.uint8)))
-    ws[CTRL_OFFSET:CTRL_OFFSET + 8].copy_(torch.from_numpy(np.array([E], np.uint64).view(np.uint8)))
     announce("stale slots tagged with the last completed epoch")
-    for rep in range(3):
-        out = _into(bf16_to_dev(x), ws)
+    for rep, xi in enumerate([x, tiny, x]):
+        out = _into(bf16_to_dev(xi), ws)
         torch.cuda.synchronize()
-        _assert_oracle(x, out, f"rep {rep}")
-    ctrl = to_np(ws[CTRL_OFFSET:CTRL_OFFSET + 16]).view(np.uint64)
-    assert ctrl[0] == E + 3 and ctrl[1] == 0          # three calls completed, no arrival pending
+        _assert_oracle(xi, out, f"rep {rep}")
+        tags = to_np(ws[:SLOTS_BYTES]).view(np.uint64) >> np.uint64(16)
+        assert np.all(tags == np.uint64(E + 1 + rep)), rep      # every slot stamped
 
 
 def test_workspace_shared_by_every_kind_of_call():
