@@ -358,7 +358,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t *red) {
 
 constexpr int kResThreads = 1024;            // one workgroup per CU
 constexpr int kStreamU = 2;                   // streamed blocks per thread per round
-constexpr int kLdsBlocks = 4;                 // STREAM: resident blocks per thread held in LDS (128 KB)
+constexpr int kLdsBlocks = 4;                 // LDS-resident blocks per thread (128 KB): STREAM 4, PAIRLDS 2 per tensor
 
 // This thread's part of the |x| maximum of workgroup p's share of a tensor
 // (the blocks that workgroup p loads, including its streamed chunks): read by
@@ -417,9 +417,14 @@ __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
 // and once more to encode (from the MALL when it fits there).  Only that
 // remainder is read twice, where the two-pass kernels read the whole tensor
 // twice.
-template <int NJ, int UMAX, bool ADAPT, bool STREAM = false>
+// PAIRLDS (a K/V pair, UMAX = 4, u <= 4 + kLdsBlocks/2): blocks 4 and 5 of each
+// tensor are held in LDS the same way, so a pair of up to ~100 MB (the pages'
+// 8-frame KV chunk of 7040 tokens x 24 heads x 128) is read once; K's LDS
+// blocks are centred when they are first read back and stored back centred.
+template <int NJ, int UMAX, bool ADAPT, bool STREAM = false, bool PAIRLDS = false>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
                                                                 int u, uint64_t wait_ticks) {
+  static_assert(!PAIRLDS || (NJ == 2 && !STREAM), "LDS-resident pairs are K/V pairs");
   const int k = blockIdx.x, nwg = gridDim.x;
   // the call's epoch: one more than the largest tag of this workgroup's slots
   uint64_t epoch = 0;
@@ -431,28 +436,34 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
   epoch = (epoch + 1) & kEpochMask;
   if (epoch == 0) epoch = 1;
   constexpr int NW = kResThreads / 64;
-  constexpr int ULDS = STREAM ? kLdsBlocks : 0;
+  constexpr bool LDSRES = STREAM || PAIRLDS;
+  constexpr int ULDS = LDSRES ? kLdsBlocks / NJ : 0;     // LDS-resident blocks per thread per tensor
   __shared__ uint32_t red[NJ][NW], red2[NJ][NW];
   __shared__ uint64_t miss[NJ][NW];
-  // LDS-resident blocks, [block][half][thread]: each wave's 16-byte stores and
-  // loads cover consecutive addresses
-  __shared__ u32x4 lds_blk[STREAM ? 2 * kLdsBlocks * kResThreads : 1];
+  // LDS-resident blocks, [tensor·ULDS + block][half][thread]: each wave's
+  // 16-byte stores and loads cover consecutive addresses
+  __shared__ u32x4 lds_blk[LDSRES ? 2 * kLdsBlocks * kResThreads : 1];
 
   // LDS-resident blocks: loaded straight into LDS (no registers held), lane
   // l of a wave into slot l of the wave's 64-slot run; lanes past the tensor
   // load nothing, and their slots are never read
-  if constexpr (STREAM) {
-    const QuantTensor &T = args.t[0];
+  if constexpr (LDSRES) {
     [[maybe_unused]] const int wave_base = threadIdx.x & ~63;          // device pass only
 #pragma unroll
-    for (int i = 0; i < ULDS; ++i) {
-      const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + threadIdx.x;
-      if (UMAX + i < u && b < 2 * T.units) {
-        [[maybe_unused]] const u32x4 *p = block_src(T, b);
+    for (int j = 0; j < NJ; ++j) {
+      const QuantTensor &T = args.t[j];
+#pragma unroll
+      for (int i = 0; i < ULDS; ++i) {
+        const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + threadIdx.x;
+        [[maybe_unused]] const int slot = j * ULDS + i;
+        if (UMAX + i < u && b < 2 * T.units) {
+          [[maybe_unused]] const u32x4 *p = block_src(T, b);
 #if defined(__HIP_DEVICE_COMPILE__)      // device-only builtin; the host pass only parses the kernel
-        __builtin_amdgcn_global_load_lds(p, &lds_blk[(2 * i) * kResThreads + wave_base], 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(p + 1, &lds_blk[(2 * i + 1) * kResThreads + wave_base], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(p, &lds_blk[(2 * slot) * kResThreads + wave_base], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(p + 1, &lds_blk[(2 * slot + 1) * kResThreads + wave_base], 16, 0,
+                                           0);
 #endif
+        }
       }
     }
   }
@@ -488,7 +499,9 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
       }
   }
   // streamed blocks (STREAM): b = nwg·u·1024 + (s·nwg + k)·1024 + thread
-  uint32_t ms = 0, ml = 0;
+  uint32_t ms = 0, ml[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) ml[j] = 0;
   if constexpr (STREAM) {
     const QuantTensor &T = args.t[0];
     const int64_t nb = 2 * T.units, cstride = (int64_t)nwg * kResThreads;
@@ -511,25 +524,39 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
         ms = ms > am ? ms : am;
       }
     }
+  }
+  if constexpr (LDSRES) {
     // every load of this wave has landed (the direct-to-LDS ones included)
 #if defined(__HIP_DEVICE_COMPILE__)
     __builtin_amdgcn_s_waitcnt(0);
 #endif
 #pragma unroll
-    for (int i = 0; i < ULDS; ++i) {
-      const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + threadIdx.x;
-      if (UMAX + i < u && b < nb) {
-        const u32x4 lo4 = lds_blk[(2 * i) * kResThreads + threadIdx.x];
-        const u32x4 hi4 = lds_blk[(2 * i + 1) * kResThreads + threadIdx.x];
-        const uint32_t wv[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-        const uint32_t am = absmax16(wv);
-        ml = ml > am ? ml : am;
+    for (int j = 0; j < NJ; ++j) {
+      const QuantTensor &T = args.t[j];
+#pragma unroll
+      for (int i = 0; i < ULDS; ++i) {
+        const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + threadIdx.x;
+        const int slot = j * ULDS + i;
+        if (UMAX + i < u && b < 2 * T.units) {
+          u32x4 lo4 = lds_blk[(2 * slot) * kResThreads + threadIdx.x];
+          u32x4 hi4 = lds_blk[(2 * slot + 1) * kResThreads + threadIdx.x];
+          uint32_t wv[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
+          if constexpr (PAIRLDS) {
+            if (T.center != nullptr) {            // K-smoothing: stored back centred
+              center_block(T, b, wv);
+              lds_blk[(2 * slot) * kResThreads + threadIdx.x] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+              lds_blk[(2 * slot + 1) * kResThreads + threadIdx.x] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            }
+          }
+          const uint32_t am = absmax16(wv);
+          ml[j] = ml[j] > am ? ml[j] : am;
+        }
       }
     }
   }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    uint32_t m = STREAM ? (ms > ml ? ms : ml) : 0u;
+    uint32_t m = ms > ml[j] ? ms : ml[j];
 #pragma unroll
     for (int i = 0; i < UMAX; ++i) {
       const uint32_t am = absmax16(w[j][i]);
@@ -629,8 +656,8 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
         scales[b] = (uint8_t)S;
       }
     }
-    if constexpr (STREAM) {
-      const int64_t nb = 2 * T.units, cstride = (int64_t)nwg * kResThreads;
+    if constexpr (LDSRES) {
+      const int64_t nb = 2 * T.units;
       // the thread index made opaque, so these indices are recomputed here
       // instead of being kept in registers (spilled) since the prologue
       uint32_t tid = threadIdx.x;
@@ -638,8 +665,9 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
 #pragma unroll
       for (int i = 0; i < ULDS; ++i) {
         const int64_t b = ((int64_t)k * u + UMAX + i) * kResThreads + tid;
-        const u32x4 lo4 = lds_blk[(2 * i) * kResThreads + tid];
-        const u32x4 hi4 = lds_blk[(2 * i + 1) * kResThreads + tid];
+        const int slot = j * ULDS + i;
+        const u32x4 lo4 = lds_blk[(2 * slot) * kResThreads + tid];
+        const u32x4 hi4 = lds_blk[(2 * slot + 1) * kResThreads + tid];
         const uint32_t wv[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
         uint32_t lo, hi;
         const uint32_t S = encode_any<ADAPT>(wv, absmax16(wv), b6, b4, lo, hi);
@@ -648,6 +676,9 @@ __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
           scales[b] = (uint8_t)S;
         }
       }
+    }
+    if constexpr (STREAM) {
+      const int64_t nb = 2 * T.units, cstride = (int64_t)nwg * kResThreads;
       const int64_t chunk0 = cstride * u + (int64_t)k * kResThreads + threadIdx.x;
       for (int64_t b0 = chunk0; b0 < nb; b0 += kStreamU * cstride) {
         uint32_t v[kStreamU][8];
@@ -682,11 +713,12 @@ struct ResidentLimits {
   int cus = 0;
   bool fits[2][2][4] = {};                // [ADAPT][NJ - 1][log2 UMAX]
   bool fits_stream[2] = {};               // [ADAPT]: the STREAM kernel (one tensor, UMAX 8)
+  bool fits_pair[2] = {};                 // [ADAPT]: the PAIRLDS kernel (K/V, UMAX 4 + LDS)
 };
 
-template <int NJ, int UMAX, bool ADAPT, bool STREAM = false>
+template <int NJ, int UMAX, bool ADAPT, bool STREAM = false, bool PAIRLDS = false>
 static const void *resident_fn() {
-  return reinterpret_cast<const void *>(&k_quant_resident<NJ, UMAX, ADAPT, STREAM>);
+  return reinterpret_cast<const void *>(&k_quant_resident<NJ, UMAX, ADAPT, STREAM, PAIRLDS>);
 }
 
 static const ResidentLimits &resident_limits() {
@@ -721,6 +753,12 @@ static const ResidentLimits &resident_limits() {
       r.fits_stream[a] = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, sfns[a], kResThreads, 0) ==
                              hipSuccess && n >= 1;
     }
+    const void *pfns[2] = {resident_fn<2, 4, false, false, true>(), resident_fn<2, 4, true, false, true>()};
+    for (int a = 0; a < 2; ++a) {
+      int n = 0;
+      r.fits_pair[a] = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pfns[a], kResThreads, 0) ==
+                           hipSuccess && n >= 1;
+    }
     filled[dev] = true;
   }
   return table[dev];
@@ -741,6 +779,15 @@ static bool launch_resident(QuantArgs &a, int njobs, int64_t max_units, hipStrea
   int li = 0;
   while (li < 4 && (1 << li) < u) ++li;
   const uint64_t wt = g_wait_ticks.load();
+  if (njobs == 2 && u > 4 && u <= 4 + kLdsBlocks / 2) {
+    // a K/V pair beyond the registers: 4 blocks per thread per tensor in
+    // registers and 2 in LDS (an 8-frame chunk of 7040 tokens fits)
+    if (!lim.fits_pair[ADAPT]) return false;
+    hipLaunchKernelGGL((k_quant_resident<2, 4, ADAPT, false, true>), dim3((unsigned)nwg), dim3(kResThreads),
+                       0, stream, a, (int)u, wt);
+    *err = hipGetLastError();
+    return true;
+  }
   if (li == 4) {
     // more than the grid's registers hold: keep 8 blocks per thread resident
     // in registers and kLdsBlocks in LDS, and stream the rest (one tensor

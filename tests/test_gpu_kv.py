@@ -126,6 +126,36 @@ def test_eight_frame_chunks(adaptive):
     assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
 
 
+def test_eight_frame_chunk_lds_resident_expired_wait_strided():
+    # An 8-frame chunk (7040 tokens x 24 heads x 128) is larger than the
+    # registers of the single-launch K/V kernel hold; it keeps two blocks per
+    # thread and tensor in LDS.  K and V are the column slices of fused QKV
+    # rows (token stride 3·H·D).  The first append's waits all expire, so its
+    # workgroups read the shares they have not heard from in global memory;
+    # the second append uses the normal wait on other data.  Every byte is
+    # compared with the oracle.
+    H, D, T = 24, 128, 7040
+    L = nv.lib()
+    prev = L.nvfp4_testing_set_quantize_wait(0)
+    L.nvfp4_testing_set_quantize_wait(prev)
+    gpu = nv.KVCache(2 * T, H, D, max_chunks=2)
+    ref = oracle.KVCacheRef(2 * T, H, D)
+    try:
+        for rep, (seed, sigma) in enumerate([(41, 2.0), (42, 0.25)]):
+            rows = workloads.random_matrix(seed, T, 3 * H * D, sigma=sigma, outliers=True)
+            announce(f"kv 7040-token LDS-resident append from fused rows, rep {rep}, wait {'0' if rep == 0 else 'default'}")
+            dev_rows = bf16_to_dev(rows)
+            L.nvfp4_testing_set_quantize_wait(0 if rep == 0 else prev)
+            gpu.append(dev_rows[:, H * D:2 * H * D], dev_rows[:, 2 * H * D:])
+            torch.cuda.synchronize()
+            del dev_rows
+            ref.append(np.ascontiguousarray(rows[:, H * D:2 * H * D]).reshape(T, H, D),
+                       np.ascontiguousarray(rows[:, 2 * H * D:]).reshape(T, H, D))
+    finally:
+        L.nvfp4_testing_set_quantize_wait(prev)
+    _compare_cache(gpu, ref, 2 * T)
+
+
 def test_strided_append_from_fused_rows():
     # K and V read in place as column slices of a [T, 3·H·D] row-major matrix
     # (the layout of a fused QKV projection output), token stride 3·H·D
