@@ -8,6 +8,9 @@
 * the pages' configuration at full size: 65536 tokens in 8-frame chunks of
   7040 tokens, K-smoothing and adaptive scales, every chunk and the whole
   read-back bit-exact;
+* single appends at the boundaries of the single launch's register and LDS
+  capacity for a K/V pair (one or both LDS blocks per thread in use, and just
+  past them, where the two-pass kernels take over);
 * keys read in place as the K slice of a fused QKV output, and
   nvfp4_qkv_append on a smoothed cache equal to nvfp4_linear followed by the
   smoothed append;
@@ -116,6 +119,34 @@ def test_eight_frame_chunks_smoothed_adaptive_full_size():
     for i in range(len(sizes)):
         ref.append(K[starts[i]:starts[i + 1]], V[starts[i]:starts[i + 1]], adaptive46=True)
     _compare(gpu, ref, T)
+    rk, rv = ref.dequant(0, T)
+    assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
+
+
+@pytest.mark.parametrize("T,smooth,adaptive", [(6000, True, False), (8192, True, True), (8192, False, False),
+                                                (8200, True, False)])
+def test_pair_register_and_lds_capacity_boundaries(T, smooth, adaptive):
+    # A K/V append of 24 heads x 128 past the registers of the single launch:
+    # 6000 tokens use one of the two LDS blocks per thread and tensor, 8192
+    # fill both exactly, 8200 go to the two-pass kernels.  Keys with channel
+    # offsets, with and without K-smoothing; every byte, the centres and the
+    # read-back bit-exact.
+    H, D = 24, 128
+    k, v = _offset_keys(60 + T, T, H, D)
+    announce(f"K/V pair at the capacity boundary: {T} tokens, smooth={smooth}, adaptive={adaptive}")
+    gpu = nv.KVCache(T, H, D, max_chunks=1, smooth_k=smooth)
+    gpu.append(bf16_to_dev(k), bf16_to_dev(v), adaptive46=adaptive)
+    ko, vo = gpu.dequant(0, T)
+    torch.cuda.synchronize()
+    ref = oracle.KVCacheRef(T, H, D, smooth_k=smooth)
+    ref.append(k, v, adaptive46=adaptive)
+    if smooth:
+        _compare(gpu, ref, T)
+    else:
+        for a, b in ((gpu.k_codes, ref.k_codes), (gpu.v_codes, ref.v_codes), (gpu.k_scales, ref.k_scales),
+                     (gpu.v_scales, ref.v_scales)):
+            assert np.array_equal(to_np(a)[:T], b[:T])
+        assert np.array_equal(to_np(gpu.gscale)[:1], np.array(ref.gscale, dtype=np.float32).reshape(-1, 2))
     rk, rv = ref.dequant(0, T)
     assert np.array_equal(to_bits(ko), rk) and np.array_equal(to_bits(vo), rv)
 
