@@ -495,14 +495,18 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
     // it O and l) moves only when some query of the wave sees a scaled score
     // more than 2^kLazy above it, so p = 2^(s·g_K − m) stays below 2^kLazy.
     // Any reference gives the same result: O and l carry the same factor, and
-    // the split merge uses m.  Keys past the split (only in its last tile)
-    // score −inf.
+    // the split merge uses m.  The exponent t = s·g_K − m is formed by one FMA
+    // (before the first reference, t = s·g_K); the tile's largest t decides
+    // whether m moves, and a move shifts t by the same amount.  Keys past the
+    // split (only in its last tile) score −inf.
     const int kvalid = (j1 - jt) < kAK ? (int)(j1 - jt) : kAK;
+    const bool no_ref = m == -__builtin_huge_valf();
+    const float off = no_ref ? 0.0f : -m;
     float mt = -__builtin_huge_valf();
     if constexpr (SMOOTH) {
       if (one_append) {
         // one append holds the tile: the term q·μ of the scaled score
-        const float bq = L.bq[scl][threadIdx.x];
+        const float bq = L.bq[scl][threadIdx.x] + off;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -546,7 +550,8 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
             const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[key0]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const float tv = key0 + e < kvalid ? s[kb][4 * g4 + e] * gk4[e] : -__builtin_huge_valf();
+              const float tv = key0 + e < kvalid ? __builtin_fmaf(s[kb][4 * g4 + e], gk4[e], off)
+                                                 : -__builtin_huge_valf();
               s[kb][4 * g4 + e] = tv;
               mt = __builtin_fmaxf(mt, tv);
             }
@@ -560,7 +565,7 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
           const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[32 * kb + 8 * g4 + 4 * hh]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float tv = s[kb][4 * g4 + e] * gk4[e];
+            const float tv = __builtin_fmaf(s[kb][4 * g4 + e], gk4[e], off);
             s[kb][4 * g4 + e] = tv;
             mt = __builtin_fmaxf(mt, tv);
           }
@@ -574,29 +579,36 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
           const f32x4 gk4 = *reinterpret_cast<const f32x4 *>(&B.gk[key0]);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float tv = key0 + e < kvalid ? s[kb][4 * g4 + e] * gk4[e] : -__builtin_huge_valf();
+            const float tv = key0 + e < kvalid ? __builtin_fmaf(s[kb][4 * g4 + e], gk4[e], off)
+                                               : -__builtin_huge_valf();
             s[kb][4 * g4 + e] = tv;
             mt = __builtin_fmaxf(mt, tv);
           }
         }
     }
     mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32, 64));
-    if (__builtin_amdgcn_ballot_w64(mt > m + kLazy) != 0) {
-      const float m_new = __builtin_fmaxf(m, mt);
-      const float alpha = m == m_new ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+    if (__builtin_amdgcn_ballot_w64(no_ref || mt > kLazy) != 0) {
+      // before the first reference mt is the largest s·g_K itself (finite:
+      // the first key of a split's first tile is always valid)
+      const float d = no_ref ? mt : __builtin_fmaxf(mt, 0.0f);
+      const float alpha = no_ref ? 1.0f : __builtin_amdgcn_exp2f(-d);
       l *= alpha;
-      m = m_new;
+      m = no_ref ? d : m + d;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][v] -= d;
     }
     float psum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pv = __builtin_amdgcn_exp2f(s[kb][v] - m);
+        const float pv = __builtin_amdgcn_exp2f(s[kb][v]);
         s[kb][v] = pv;
         psum += pv;
       }
