@@ -14,7 +14,13 @@
 // the order in which the parts are added.  The workspace needs no
 // initialisation: every partial sum is written before it is read.
 //
-// Two launches before the append's quantiser:
+// Short chunks (at most kDirectMaxT tokens: one frame, the tail of a
+// sequence) take one launch before the append's quantiser:
+//   k_kv_center_direct — 16 channels per 1024-thread workgroup: every lane
+//                  sums 8 channels over every 512th token (exact binary64),
+//                  the 512 token rows meet in LDS as 64-bit integers, and
+//                  one thread per channel turns the sum into μ.
+// Longer chunks take two:
 //   k_kv_colsum  — workgroups own a strip of tokens (sized so that about 1024
 //                  workgroups cover the chunk) x 512 channels; every lane sums
 //                  8 channels over every fourth token of the strip (16-byte
@@ -38,6 +44,10 @@ constexpr int kSmChan = 512;              // channels per colsum workgroup (64 l
 constexpr int kSmRows = kSmThreads / 64;  // token rows per colsum workgroup
 constexpr int kSmUnroll = 4;              // loads of a lane in flight together
 constexpr int kSmTargetWgs = 1024;        // colsum workgroups aimed at (four per CU)
+constexpr int kDirThreads = 1024;         // k_kv_center_direct: 2 lanes x 8 channels x 512 token rows
+constexpr int kDirChan = 16;              // channels per k_kv_center_direct workgroup
+constexpr int kDirRows = kDirThreads / (kDirChan / 8);
+constexpr int64_t kDirectMaxT = 2304;     // longest chunk summed by k_kv_center_direct
 
 // Tokens per colsum strip: a multiple of 16 (4 rows x 4 loads in flight),
 // long enough that about kSmTargetWgs workgroups cover the chunk.
@@ -150,6 +160,55 @@ __global__ void __launch_bounds__(kSmThreads) k_kv_center(SmoothArgs a, int64_t 
   a.center[c] = bf16_rne_from_f64(mean * 0x1p-24);
 }
 
+// Sum and centre in one launch for a short chunk: workgroup x owns channels
+// 16x .. 16x+15; thread (row = t/2, octet o = t%2) adds channels 16x+8o .. +7
+// of tokens row, row + 512, ... in binary64 (at most 5 values of magnitude
+// <= 2^38 per lane: exact), then the rows meet in LDS as 64-bit integers.
+__global__ void __launch_bounds__(kDirThreads) k_kv_center_direct(SmoothArgs a) {
+  __shared__ int64_t red[kDirRows][kDirChan];
+  __shared__ int64_t red2[32][kDirChan];
+  const int oct = threadIdx.x % (kDirChan / 8), row = threadIdx.x / (kDirChan / 8);
+  const int64_t c0 = (int64_t)blockIdx.x * kDirChan + 8 * oct;
+  double accd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (c0 < a.e) {
+    for (int64_t tb = row; tb < a.T; tb += (int64_t)kDirRows * kSmUnroll) {
+      u32x4 v[kSmUnroll];
+#pragma unroll
+      for (int i = 0; i < kSmUnroll; ++i) {
+        const int64_t t = tb + (int64_t)kDirRows * i;
+        v[i] = t < a.T ? *reinterpret_cast<const u32x4 *>(a.k + t * a.ld + c0) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < kSmUnroll; ++i) {
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          accd[2 * k] += (double)grid_steps_f32(w[k] & 0xFFFFu);   // +0 steps for the padding zeros
+          accd[2 * k + 1] += (double)grid_steps_f32(w[k] >> 16);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) red[row][8 * oct + k] = (int64_t)accd[k];
+  __syncthreads();
+  if (threadIdx.x < 32 * kDirChan) {       // 32 parts of kDirRows/32 rows per channel
+    const int c = threadIdx.x % kDirChan, part = threadIdx.x / kDirChan;
+    int64_t S = 0;
+#pragma unroll
+    for (int r = 0; r < kDirRows / 32; ++r) S += red[part * (kDirRows / 32) + r][c];
+    red2[part][c] = S;
+  }
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * kDirChan + threadIdx.x;
+  if (threadIdx.x >= kDirChan || c >= a.e) return;
+  int64_t S = 0;                           // exact: |S| <= 2^38 · 2304
+#pragma unroll
+  for (int p = 0; p < 32; ++p) S += red2[p][threadIdx.x];
+  const double mean = (double)S / (double)a.T;
+  a.center[c] = bf16_rne_from_f64(mean * 0x1p-24);
+}
+
 int64_t smooth_partial_count(int64_t T, int64_t e) {
   const int64_t strip = smooth_strip(T, e);
   return (T + strip - 1) / strip * e;
@@ -157,6 +216,12 @@ int64_t smooth_partial_count(int64_t T, int64_t e) {
 
 hipError_t launch_kv_smooth(const SmoothArgs &a, hipStream_t stream) {
   if (a.T < 1 || a.e < 8 || a.e % 8) return hipErrorInvalidValue;
+  if (a.T <= kDirectMaxT) {
+    const int64_t groups = (a.e + kDirChan - 1) / kDirChan;
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_kv_center_direct, dim3((unsigned)groups), dim3(kDirThreads), 0, stream, a);
+    return hipGetLastError();
+  }
   const int64_t strip = smooth_strip(a.T, a.e);
   const int64_t strips = (a.T + strip - 1) / strip, cgroups = (a.e + kSmChan - 1) / kSmChan;
   if (strips > 0x7FFFFFFF || cgroups > 65535) return hipErrorInvalidValue;
