@@ -160,15 +160,20 @@ __global__ void __launch_bounds__(kSmThreads) k_kv_center(SmoothArgs a, int64_t 
   a.center[c] = bf16_rne_from_f64(mean * 0x1p-24);
 }
 
-// Sum and centre in one launch for a short chunk: workgroup x owns channels
-// 16x .. 16x+15; thread (row = t/2, octet o = t%2) adds channels 16x+8o .. +7
+// Sum and centre in one launch for a short chunk: channel group x (16
+// channels, 16x .. 16x+15) goes to workgroup 8·(x mod n/8) + x div (n/8)
+// when the n groups split evenly over the 8 XCDs (workgroup w runs on XCD
+// w mod 8), so the four groups that share a 128-byte line of a token row are
+// read on one XCD and its L2 fetches the line once; thread (row = t/2, octet o = t%2) adds channels 16x+8o .. +7
 // of tokens row, row + 512, ... in binary64 (at most 5 values of magnitude
 // <= 2^38 per lane: exact), then the rows meet in LDS as 64-bit integers.
 __global__ void __launch_bounds__(kDirThreads) k_kv_center_direct(SmoothArgs a) {
   __shared__ int64_t red[kDirRows][kDirChan];
   __shared__ int64_t red2[32][kDirChan];
   const int oct = threadIdx.x % (kDirChan / 8), row = threadIdx.x / (kDirChan / 8);
-  const int64_t c0 = (int64_t)blockIdx.x * kDirChan + 8 * oct;
+  const int64_t n = gridDim.x, w = blockIdx.x;
+  const int64_t grp = (n % 8 == 0) ? (w % 8) * (n / 8) + w / 8 : w;
+  const int64_t c0 = grp * kDirChan + 8 * oct;
   double accd[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   if (c0 < a.e) {
     for (int64_t tb = row; tb < a.T; tb += (int64_t)kDirRows * kSmUnroll) {
@@ -200,7 +205,7 @@ __global__ void __launch_bounds__(kDirThreads) k_kv_center_direct(SmoothArgs a) 
     red2[part][c] = S;
   }
   __syncthreads();
-  const int64_t c = (int64_t)blockIdx.x * kDirChan + threadIdx.x;
+  const int64_t c = grp * kDirChan + threadIdx.x;
   if (threadIdx.x >= kDirChan || c >= a.e) return;
   int64_t S = 0;                           // exact: |S| <= 2^38 · 2304
 #pragma unroll
