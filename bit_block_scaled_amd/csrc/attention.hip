@@ -384,8 +384,17 @@ __global__ void __launch_bounds__(kAThreads, 2) k_attention(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds<SMOOTH> L;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 31, hh = lane >> 5;
-  const int h = blockIdx.y, split = blockIdx.z;
-  const int64_t q = (int64_t)blockIdx.x * kAQ + 32 * w + r;       // this lane's query
+  // Work item (query block, head, split) of this workgroup, query block
+  // fastest: the workgroups of one (head, split) read the same key tiles, so
+  // consecutive items go to one XCD (workgroup i of a 1-D grid runs on XCD
+  // i mod 8) when the grid splits evenly over the 8 XCDs, and their tiles
+  // are fetched into that XCD's L2 once.
+  const int64_t nwg = gridDim.x, wid = blockIdx.x;
+  const int64_t item = (nwg % 8 == 0) ? (wid % 8) * (nwg / 8) + wid / 8 : wid;
+  const int64_t nqb = (a.Tq + kAQ - 1) / kAQ;
+  const int qb = (int)(item % nqb);
+  const int h = (int)((item / nqb) % a.heads), split = (int)(item / (nqb * a.heads));
+  const int64_t q = (int64_t)qb * kAQ + 32 * w + r;               // this lane's query
   const int64_t qc = q < a.Tq ? q : a.Tq - 1;
   const int64_t j0 = (int64_t)split * a.keys_per_split;
   const int64_t j1 = (j0 + a.keys_per_split < a.Tk) ? j0 + a.keys_per_split : a.Tk;
@@ -733,7 +742,9 @@ int64_t attention_keys_per_split(int64_t Tk, int64_t nsplit) {
 }
 
 hipError_t launch_attention(const AttnArgs &a, bool bf16, hipStream_t stream) {
-  const dim3 grid((unsigned)((a.Tq + kAQ - 1) / kAQ), (unsigned)a.heads, (unsigned)a.nsplit);
+  const int64_t items = (a.Tq + kAQ - 1) / kAQ * a.heads * a.nsplit;
+  if (items > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)items);
   if (bf16)
     hipLaunchKernelGGL((k_attention<true, false>), grid, dim3(kAThreads), 0, stream, a);
   else if (a.kcenter != nullptr)
