@@ -36,6 +36,12 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int64_t kMaxElements = int64_t(1) << 36;   // keeps unit indices below 2^31
 constexpr size_t kQuantWs = nvfp4::kQuantScratchBytes;
+// Every workspace starts with the same head: the scratch of two quantised
+// tensors (regions 0 and 1), written only by the quantiser (its slots and its
+// two-pass partial maxima); every other buffer of a workspace lies after it.
+// So one zeroed buffer can serve calls of any kind and size: no call writes
+// data where another keeps quantiser slots.
+constexpr size_t kWsHead = 2 * kQuantWs;
 
 int check_mk(int64_t M, int64_t K, const char *who) {
   if (M < 1) return fail(NVFP4_EINVAL, std::string(who) + ": M must be >= 1");
@@ -74,19 +80,19 @@ int launched(hipError_t e, hipStream_t st, const char *who) {
   return s;
 }
 
-// nvfp4_linear workspace: [codes | scales | gscale | amax partials]
+// nvfp4_linear workspace: [head (quantiser scratch of x in region 0) | codes | scales | gscale]
 struct LinearWs {
-  size_t codes, scales, gscale, partials, total;
+  size_t partials, codes, scales, gscale, total;
 };
 
 LinearWs linear_ws(int64_t M, int64_t K) {
   LinearWs w;
   const size_t n = size_t(M) * size_t(K);
-  w.codes = 0;
+  w.partials = 0;
+  w.codes = kWsHead;
   w.scales = round_up(w.codes + n / 2, 256);
   w.gscale = round_up(w.scales + n / 16, 256);
-  w.partials = round_up(w.gscale + sizeof(float), 256);
-  w.total = round_up(w.partials + kQuantWs, 256);
+  w.total = round_up(w.gscale + sizeof(float), 256);
   return w;
 }
 
@@ -432,11 +438,12 @@ int nvfp4_kv_append(nvfp4_kv_cache *c, const uint16_t *K, const uint16_t *V, int
   return nvfp4_kv_append_ex(c, K, V, T, ld, 0u, ws, ws_bytes, stream);
 }
 
-// nvfp4_qkv_append workspace: [linear workspace | tile maxima | append scratch]
-// (the append scratch serves the unfused fallback)
+// nvfp4_qkv_append workspace: [linear workspace | tile maxima]; the append of
+// K and V (the unfused fallback) uses regions 0 and 1 of the head, after the
+// quantisation of x in region 0 is done
 struct QkvWs {
   LinearWs lin;
-  size_t slots, app, total;
+  size_t slots, total;
   int64_t max_tiles;
 };
 
@@ -445,8 +452,7 @@ static QkvWs qkv_ws(int64_t T, int64_t N, int64_t D) {
   w.lin = linear_ws(T, D);
   w.max_tiles = ((T + 127) / 128) * ((N + 127) / 128);   // the finest tiling the GEMM uses
   w.slots = w.lin.total;
-  w.app = round_up(w.slots + size_t(w.max_tiles) * sizeof(uint32_t), 256);
-  w.total = round_up(w.app + 2 * kQuantWs, 256);
+  w.total = round_up(w.slots + size_t(w.max_tiles) * sizeof(uint32_t), 256);
   return w;
 }
 
@@ -504,10 +510,10 @@ int nvfp4_qkv_append(nvfp4_kv_cache *c, const uint16_t *x, int64_t T, int64_t D,
       (s = enqueue_smoothing(c, QKV + hd, T, N, base, w.total, st, "qkv_append/smooth", &center)))
     return s;
   nvfp4::QuantJob jobs[2] = {
-      {QKV + hd, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, base + w.app, T, hd, N,
+      {QKV + hd, c->k_codes + off / 2, c->k_scales + off / 16, c->gscale + 2 * c->n_chunks, base, T, hd, N,
        center},
       {QKV + 2 * hd, c->v_codes + off / 2, c->v_scales + off / 16, c->gscale + 2 * c->n_chunks + 1,
-       base + w.app + kQuantWs, T, hd, N}};
+       base + kQuantWs, T, hd, N}};
   const nvfp4::ChunkMark mark{c->chunk_start, c->n_chunks + 1, c->n_tokens + T};
   const bool adapt = (qflags & NVFP4_Q_ADAPTIVE_4_6) != 0;
   if (fused) {
@@ -558,7 +564,8 @@ static size_t attention_ws_bytes(int64_t Tq, int64_t heads, int64_t Tk) {
   const int64_t nsplit = (Tk + kps - 1) / kps;
   if (nsplit <= 1) return 0;
   const size_t rows = size_t(nsplit) * size_t(Tq) * size_t(heads);
-  return round_up(rows * 128 * sizeof(float), 256) + round_up(rows * 2 * sizeof(float), 256);
+  // the split results after the common head
+  return kWsHead + round_up(rows * 128 * sizeof(float), 256) + round_up(rows * 2 * sizeof(float), 256);
 }
 
 static int check_attn_common(const uint16_t *Q, int64_t Tq, int64_t ldq, int64_t heads, uint16_t *O,
@@ -590,8 +597,9 @@ static int run_attention(nvfp4::AttnArgs &a, bool bf16, float scale, void *ws, s
     int s;
     if ((s = check_ptr(ws, "ws"))) return s;
     const size_t rows = size_t(a.nsplit) * size_t(a.Tq) * size_t(a.heads);
-    a.part_o = static_cast<float *>(ws);
-    a.part_ml = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + round_up(rows * 128 * sizeof(float), 256));
+    uint8_t *parts = static_cast<uint8_t *>(ws) + kWsHead;
+    a.part_o = reinterpret_cast<float *>(parts);
+    a.part_ml = reinterpret_cast<float *>(parts + round_up(rows * 128 * sizeof(float), 256));
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   return launched(nvfp4::launch_attention(a, bf16, st), st, who);
@@ -601,7 +609,7 @@ int nvfp4_quantize_rht_workspace(int64_t T, int64_t N, size_t *bytes) {
   if (bytes == nullptr) return fail(NVFP4_EINVAL, "bytes is NULL");
   if (T < 32 || T % 32) return fail(NVFP4_EINVAL, "quantize_rht_workspace: T must be a positive multiple of 32");
   if (N < 1 || N > kMaxElements / T) return fail(NVFP4_EINVAL, "quantize_rht_workspace: bad N");
-  *bytes = 4 * size_t(nvfp4::kRhtMaxParts);
+  *bytes = kWsHead + 4 * size_t(nvfp4::kRhtMaxParts);     // partial maxima after the common head
   return NVFP4_OK;
 }
 
@@ -620,7 +628,8 @@ int nvfp4_quantize_rht(const uint16_t *x, int64_t T, int64_t N, int64_t ldx, uin
   if ((s = check_ptr(gscale, "gscale", 4))) return s;
   if (ws == nullptr || ws_bytes < need) return fail(NVFP4_EWORKSPACE, "quantize_rht: workspace too small");
   if ((s = check_ptr(ws, "ws", 4))) return s;
-  nvfp4::RhtArgs a{x, T, N, ldx, sign_mask, codes, scales, gscale, static_cast<uint32_t *>(ws)};
+  nvfp4::RhtArgs a{x, T, N, ldx, sign_mask, codes, scales, gscale,
+                   reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(ws) + kWsHead)};
   hipStream_t st = static_cast<hipStream_t>(stream);
   return launched(nvfp4::launch_quantize_rht(a, st), st, "quantize_rht");
 }

@@ -78,14 +78,17 @@ extern "C" {
  * Workspace bytes nvfp4_quantize needs for an [M, K] input (scratch for the
  * tensor-amax reduction).  Writes *bytes; the size depends only on M and K.
  *
- * Workspaces of every call (quantise, linear, linear_q, KV append) must be
- * all zero before their first use (hipMemset, or a zero-filled tensor); after
- * that only the library writes them, and the caller must not change them
- * between calls.  The library keeps a call counter in them from one call to
- * the next, in device memory, so calls captured in a HIP graph stay correct on
- * every replay.  A workspace may be shared by calls of any kind and size that
- * are ordered on one stream; calls that may run at the same time need
- * separate workspaces.
+ * Workspaces of every call (quantise, linear, linear_q, KV append, QKV
+ * append, Hadamard-transformed quantise, attention) must be all zero before
+ * their first use (hipMemset, or a zero-filled tensor); after that only the
+ * library writes them, and the caller must not change them between calls.
+ * The library keeps a call counter in them from one call to the next, in
+ * device memory, so calls captured in a HIP graph stay correct on every
+ * replay.  Every workspace starts with the same 24 KiB head, the scratch of
+ * two quantised tensors, which only the quantiser writes; each call's other
+ * buffers lie after it.  So one buffer, sized for the largest of its uses,
+ * may be shared by calls of any kind and size that are ordered on one
+ * stream; calls that may run at the same time need separate workspaces.
  */
 int nvfp4_quantize_workspace(int64_t M, int64_t K, size_t *bytes);
 

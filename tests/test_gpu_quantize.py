@@ -300,3 +300,62 @@ def test_workspace_shared_by_every_kind_of_call():
         torch.cuda.synchronize()
         rc, rs, rg = oracle.quantize(x, **kw)
         assert to_np(g)[0] == rg and np.array_equal(to_np(scales), rs) and np.array_equal(to_np(codes), rc), i
+
+
+def test_one_buffer_shared_by_every_entry_point():
+    # Every workspace starts with the same head (the scratch of two quantised
+    # tensors) and keeps its other buffers after it, so one zeroed buffer can
+    # serve linear layers of different sizes, quantisation, KV appends, the
+    # QKV append, the Hadamard-transformed quantiser and attention in turn.
+    # Each result equals the same call on a workspace of its own (or the
+    # oracle), and afterwards each of the two slot regions carries one tag:
+    # no call has written data where another keeps its slots.
+    H, D, T, Dm = 24, 128, 880, 3072
+    rng_w = [workloads.random_matrix(200 + i, n, k, sigma=0.02) for i, (n, k) in
+             enumerate([(1024, 3072), (512, 1024), (3 * H * D, Dm)])]
+    wq = [nv.quantize(bf16_to_dev(w)) for w in rng_w]
+    x1 = bf16_to_dev(workloads.random_matrix(210, 512, 3072, sigma=1.0, outliers=True))
+    x2 = bf16_to_dev(workloads.random_matrix(211, 2048, 1024, sigma=2.0, outliers=True))
+    xq = workloads.random_matrix(212, 3000, 3072, sigma=0.5, outliers=True)
+    xr = workloads.random_matrix(213, 512, 3072, sigma=1.0)
+    xf = bf16_to_dev(workloads.random_matrix(214, T, Dm, sigma=1.0, outliers=True))
+    kvs = [workloads.random_matrix(215 + i, T, H * D, sigma=1.0 + i) for i in range(4)]
+    q = bf16_to_dev(workloads.random_matrix(220, 256, H * D, sigma=1.0))
+    shared = nv.KVCache(4 * T, H, D, max_chunks=8)
+    fresh = nv.KVCache(4 * T, H, D, max_chunks=8)
+    need = max(nv.linear_workspace_bytes(512, 3072), nv.linear_workspace_bytes(2048, 1024),
+               nv.quantize_workspace_bytes(3000, 3072), shared.workspace_bytes(T),
+               shared.qkv_workspace_bytes(T, Dm), nv.quantize_rht_workspace_bytes(512, 3072),
+               nv.attention_workspace_bytes(256, H, 2 * T), nv.attention_workspace_bytes(256, H, 3 * T))
+    ws = nv.workspace(need)
+    announce(f"one {need}-byte workspace for every entry point")
+    for rep in range(2):
+        for x, w in ((x1, wq[0]), (x2, wq[1])):
+            got = nv.linear(x, *w, ws=ws)
+            assert torch.equal(got, nv.linear(x, *w)), ("linear", rep, tuple(x.shape))
+        codes = torch.empty((3000, 1536), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((3000, 192), dtype=torch.uint8, device="cuda")
+        g = torch.empty((1,), dtype=torch.float32, device="cuda")
+        nv.quantize_into(bf16_to_dev(xq), codes, scales, g, ws)
+        _assert_oracle(xq, (codes, scales, g), f"quantize rep {rep}")
+        k, v = (bf16_to_dev(kvs[2 * rep]), bf16_to_dev(kvs[2 * rep + 1]))
+        shared.append(k, v, ws=ws)
+        fresh.append(k, v)
+        if rep == 0:
+            shared.qkv_append(xf, *wq[2], ws=ws)
+            fresh.qkv_append(xf, *wq[2])
+        rc, rs, rg = nv.quantize_rht(bf16_to_dev(xr), 0xA5C3, ws=ws)
+        oc, os_, og = oracle.quantize_rht(xr, 0xA5C3)
+        assert np.array_equal(to_np(rc), oc) and np.array_equal(to_np(rs), os_) and to_np(rg)[0] == og
+        n = shared.n_tokens
+        o_shared = shared.attention(q, [(0, n)], ws=ws)
+        assert torch.equal(o_shared, fresh.attention(q, [(0, n)])), ("attention", rep)
+    torch.cuda.synchronize()
+    n = shared.n_tokens
+    for a, b in ((shared.k_codes, fresh.k_codes), (shared.v_codes, fresh.v_codes),
+                 (shared.k_scales, fresh.k_scales), (shared.v_scales, fresh.v_scales)):
+        assert torch.equal(a[:n], b[:n])
+    assert torch.equal(shared.gscale[:shared.n_chunks], fresh.gscale[:fresh.n_chunks])
+    for r, off in enumerate((0, 12288)):
+        tags = to_np(ws[off:off + SLOTS_BYTES]).view(np.uint64) >> np.uint64(16)
+        assert len(set(tags.tolist())) == 1, ("slot region", r)
