@@ -14,9 +14,11 @@
 //             amax) slot and then polls all slots, so every workgroup derives
 //             A itself; then it encodes its registers, one 8-byte code store
 //             and one scale byte per block.  Used whenever the tensors fit in
-//             the registers of such a grid; a workgroup whose wait for A
-//             expires reads the shares of the workgroups it has not heard
-//             from itself, so the result does not depend on residency.
+//             the registers of such a grid (plus LDS for one large tensor,
+//             whose remainder is streamed, or for a K/V pair of up to ~100
+//             MB); a workgroup whose wait for A expires reads the shares of
+//             the workgroups it has not heard from itself, so the result does
+//             not depend on residency.
 //   two-pass  k_amax (grid-stride max of |x|, one partial per workgroup),
 //             then k_encode (every workgroup folds the partials and encodes);
 //             lanes take consecutive 16-element blocks, four per round.  Used
@@ -418,9 +420,10 @@ __device__ uint32_t share_max(const QuantTensor &T, int p, int u, int nwg) {
 // remainder is read twice, where the two-pass kernels read the whole tensor
 // twice.
 // PAIRLDS (a K/V pair, UMAX = 4, u <= 4 + kLdsBlocks/2): blocks 4 and 5 of each
-// tensor are held in LDS the same way, so a pair of up to ~100 MB (the pages'
-// 8-frame KV chunk of 7040 tokens x 24 heads x 128) is read once; K's LDS
-// blocks are centred when they are first read back and stored back centred.
+// tensor are held in LDS the same way, so a pair of up to ~100 MB (an 8-frame
+// KV chunk of 7040 tokens x 24 heads x 128, 二、方法 / 推理底座) is read once;
+// K's LDS blocks are centred when they are first read back and stored back
+// centred.
 template <int NJ, int UMAX, bool ADAPT, bool STREAM = false, bool PAIRLDS = false>
 __global__ void __launch_bounds__(kResThreads) k_quant_resident(QuantArgs args,
                                                                 int u, uint64_t wait_ticks) {
