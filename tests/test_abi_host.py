@@ -301,3 +301,24 @@ def test_qkv_append_rejects(L):
     d.n_chunks = 4
     assert f(*args) == ECAP                                  # no chunk slot
     assert d.n_tokens == 0 and d.n_chunks == 4               # unchanged on error
+
+
+def test_every_workspace_starts_with_the_quantiser_head(L):
+    # Every workspace reserves the same 24 KiB head (the quantiser scratch of
+    # two tensors) before its other buffers, so the sizes of the calls that
+    # keep more than the quantiser scratch are at least the head plus those
+    # buffers; a call without split results (one key split) needs none.
+    HEAD = 2 * (8 * 1024 + 4 * 1024)
+    n = C.c_size_t()
+    assert L.nvfp4_quantize_workspace(4096, 3072, C.byref(n)) == 0 and n.value == HEAD // 2
+    assert L.nvfp4_kv_append_workspace(880, 24, 128, C.byref(n)) == 0 and n.value == HEAD
+    assert L.nvfp4_linear_workspace(4096, 3072, C.byref(n)) == 0
+    assert n.value >= HEAD + 4096 * 3072 // 2 + 4096 * 3072 // 16
+    assert L.nvfp4_linear_q_workspace(4096, 9216, 3072, C.byref(n)) == 0
+    assert n.value >= HEAD + 4096 * 3072 * 9 // 16 + 4096 * 9216 * 2
+    assert L.nvfp4_qkv_append_workspace(880, 24, 128, 3072, C.byref(n)) == 0
+    assert n.value >= HEAD + 880 * 3072 * 9 // 16
+    assert L.nvfp4_quantize_rht_workspace(8192, 3072, C.byref(n)) == 0 and n.value > HEAD
+    assert L.nvfp4_kv_attention_workspace(880, 24, 65536, C.byref(n)) == 0
+    assert n.value >= HEAD + 2 * 880 * 24 * 128 * 4                 # several key splits
+    assert L.nvfp4_kv_attention_workspace(1, 1, 64, C.byref(n)) == 0 and n.value == 0   # one split
