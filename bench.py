@@ -610,6 +610,18 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
                 cache.dequant(a, b, kb[offs[i]:offs[i + 1]], vb[offs[i]:offs[i + 1]])
             nv.attention_bf16(qa, kb, vb, out=oa, ws=ws_a)
         tu = time_us(torch, unfused, 10, 3)
+
+        def one(fn):                     # one timed call, events on the work stream
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            return e0.elapsed_time(e1) * 1e3
+        # the same two kernels timed in alternating pairs, so both see the
+        # same clock and cache state; the ratio of each pair
+        pairs = [one(lambda: cache.attention(qa, ranges, out=oa, ws=ws_a)) /
+                 one(lambda: nv.attention_bf16(qa, kb, vb, out=oa, ws=ws_a)) for _ in range(20)]
         pn, pb, pu = float(np.median(tn)), float(np.median(tb)), float(np.median(tu))
         kernels[f"attention_{name}_nvfp4"] = {"queries": 880, "keys": Tk, "heads": 24, "us": pct(tn),
                                              "roofline": roof_gemm(flops_a, pn)}
@@ -620,6 +632,11 @@ def extras(kernels, nv, torch, np, workloads, dev, up, flush, x_ffn, lq_ws, qu):
                                                  "roofline": roof_gemm(flops_a, pb)}
         kernels[f"attention_{name}_dequant_then_bf16"] = {"us": pct(tu)}
         kernels[f"attention_{name}_nvfp4_vs_bf16"] = {"time_ratio": round(pn / pb, 4),
+                                                       "time_ratio_interleaved": {
+                                                           "p10": round(float(np.percentile(pairs, 10)), 4),
+                                                           "p50": round(float(np.median(pairs)), 4),
+                                                           "p90": round(float(np.percentile(pairs, 90)), 4),
+                                                           "n": len(pairs)},
                                                        "dequant_then_bf16_ratio": round(pu / pb, 4)}
         del ws_a
     del cache, cache_s, ko, vo, qa, oa
